@@ -1,0 +1,269 @@
+// C ABI of libdcp (declared in include/dcp.h): argument validation, work
+// planning and kernel launches.  Host code only; the kernels live in the other
+// .hip files of this directory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dcp.h"
+#include "dcp_internal.h"
+#include "dcp_params.h"
+#include "dcp_shard.h"
+
+namespace {
+
+constexpr int32_t kMaxBatch = 1 << 16;
+constexpr int32_t kMaxParts = 1 << 16;
+constexpr int32_t kMaxDevices = 64;
+
+// Read-only cache of the compute-unit count per device (filled on first use).
+int g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices) g_cu_count[dev] = cus;
+  return cus;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shape checks shared by workspace sizing and the partial call.  Fills the
+// number of head groups (work-groups per span) on success.
+dcp_status_t check_desc(const dcp_attn_desc_t* d, int32_t* head_groups) {
+  if (!d) return DCP_ERROR_INVALID_VALUE;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->block_size < 1 || d->qk_dim < 1 ||
+      d->v_dim < 1 || !(d->softmax_scale == d->softmax_scale) || isinf(d->softmax_scale))
+    return DCP_ERROR_INVALID_VALUE;
+  if (d->num_q_heads % d->num_kv_heads) return DCP_ERROR_INVALID_VALUE;
+  if (d->kind == DCP_KV_MLA_LATENT) {
+    if (d->num_kv_heads != 1) return DCP_ERROR_INVALID_VALUE;
+    if (d->qk_dim != 576 || d->v_dim != 512) return DCP_ERROR_NOT_SUPPORTED;
+    if (d->num_q_heads > 128 || d->block_size % dcp::kMlaTile) return DCP_ERROR_NOT_SUPPORTED;
+    const int hpg = dcp::mla_heads_per_group(d->num_q_heads);
+    *head_groups = (d->num_q_heads + hpg - 1) / hpg;
+    return DCP_SUCCESS;
+  }
+  if (d->kind == DCP_KV_GQA) {
+    if (d->qk_dim != 128 || d->v_dim != 128) return DCP_ERROR_NOT_SUPPORTED;
+    if (d->num_q_heads / d->num_kv_heads > 16 || d->block_size % 16) return DCP_ERROR_NOT_SUPPORTED;
+    *head_groups = d->num_kv_heads / dcp::gqa_kv_heads_per_group(d->num_kv_heads);
+    return DCP_SUCCESS;
+  }
+  return DCP_ERROR_INVALID_VALUE;
+}
+
+int32_t default_parts(int32_t head_groups) {
+  int cus = device_cu_count();
+  if (cus <= 0) cus = 256;
+  int32_t p = cus / head_groups;
+  if (head_groups > 1) p = (p / 8) * 8;  // keeps the XCD-aware block mapping
+  return p < 1 ? 1 : p;
+}
+
+struct WsLayout {
+  size_t prefix, lse, o, total;
+};
+
+WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
+  WsLayout l;
+  l.prefix = 256;
+  l.lse = l.prefix + align256(sizeof(int64_t) * ((size_t)batch + 1));
+  l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
+  l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);
+  return l;
+}
+
+dcp_status_t check_shard_args(int32_t num_ranks, int32_t interleave, int32_t rank) {
+  if (num_ranks < 1 || interleave < 1 || rank < 0 || rank >= num_ranks) return DCP_ERROR_INVALID_VALUE;
+  return DCP_SUCCESS;
+}
+
+dcp_status_t hip_status(hipError_t e) { return e == hipSuccess ? DCP_SUCCESS : DCP_ERROR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dcp_status_string(int32_t status) {
+  switch (status) {
+    case DCP_SUCCESS: return "DCP_SUCCESS";
+    case DCP_ERROR_INVALID_VALUE: return "DCP_ERROR_INVALID_VALUE";
+    case DCP_ERROR_NOT_SUPPORTED: return "DCP_ERROR_NOT_SUPPORTED";
+    case DCP_ERROR_WORKSPACE: return "DCP_ERROR_WORKSPACE";
+    case DCP_ERROR_HIP: return "DCP_ERROR_HIP";
+    default: return "DCP_ERROR_UNKNOWN";
+  }
+}
+
+dcp_status_t dcp_shard_map(const int32_t* seq_lens, int32_t batch, int32_t num_ranks,
+                           int32_t interleave, int32_t rank, int32_t* local_lens,
+                           int64_t* total_local, int32_t* max_local) {
+  dcp_status_t st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (batch < 0 || (batch > 0 && (!seq_lens || !local_lens))) return DCP_ERROR_INVALID_VALUE;
+  for (int32_t b = 0; b < batch; ++b)
+    if (seq_lens[b] < 0) return DCP_ERROR_INVALID_VALUE;
+  int64_t total = 0;
+  int32_t mx = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t lr = (int32_t)dcp_local_len(seq_lens[b], num_ranks, interleave, rank);
+    local_lens[b] = lr;
+    total += lr;
+    mx = lr > mx ? lr : mx;
+  }
+  if (total_local) *total_local = total;
+  if (max_local) *max_local = mx;
+  return DCP_SUCCESS;
+}
+
+dcp_status_t dcp_shard_locate(const int64_t* positions, int64_t count, int32_t num_ranks,
+                              int32_t interleave, int32_t* owner, int64_t* local_index) {
+  if (num_ranks < 1 || interleave < 1 || count < 0) return DCP_ERROR_INVALID_VALUE;
+  if (count > 0 && (!positions || !owner || !local_index)) return DCP_ERROR_INVALID_VALUE;
+  for (int64_t i = 0; i < count; ++i)
+    if (positions[i] < 0) return DCP_ERROR_INVALID_VALUE;
+  for (int64_t i = 0; i < count; ++i) {
+    owner[i] = dcp_owner(positions[i], num_ranks, interleave);
+    local_index[i] = dcp_local_index(positions[i], num_ranks, interleave);
+  }
+  return DCP_SUCCESS;
+}
+
+dcp_status_t dcp_shard_global(const int64_t* local_index, int64_t count, int32_t num_ranks,
+                              int32_t interleave, int32_t rank, int64_t* positions) {
+  dcp_status_t st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (count < 0 || (count > 0 && (!local_index || !positions))) return DCP_ERROR_INVALID_VALUE;
+  for (int64_t i = 0; i < count; ++i)
+    if (local_index[i] < 0) return DCP_ERROR_INVALID_VALUE;
+  for (int64_t i = 0; i < count; ++i)
+    positions[i] = dcp_global_index(local_index[i], num_ranks, interleave, rank);
+  return DCP_SUCCESS;
+}
+
+dcp_status_t dcp_shard_map_device(const int32_t* seq_lens, int32_t batch, int32_t num_ranks,
+                                  int32_t interleave, int32_t rank, int32_t* local_lens,
+                                  void* stream) {
+  dcp_status_t st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (batch < 0 || (batch > 0 && (!seq_lens || !local_lens))) return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_shard_map(seq_lens, batch, num_ranks, interleave, rank, local_lens,
+                                          (hipStream_t)stream));
+}
+
+dcp_status_t dcp_local_block_table(const int32_t* global_block_table, int32_t batch,
+                                   int32_t max_global_blocks, int32_t num_ranks,
+                                   int32_t interleave, int32_t block_size, int32_t rank,
+                                   int32_t* local_block_table, int32_t max_local_blocks,
+                                   void* stream) {
+  dcp_status_t st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (batch < 0 || max_global_blocks < 0 || max_local_blocks < 0 || block_size < 1)
+    return DCP_ERROR_INVALID_VALUE;
+  if ((int64_t)batch * max_local_blocks > 0 && (!local_block_table || (max_global_blocks > 0 && !global_block_table)))
+    return DCP_ERROR_INVALID_VALUE;
+  if (interleave % block_size) return DCP_ERROR_NOT_SUPPORTED;
+  return hip_status(dcp::launch_local_block_table(global_block_table, batch, max_global_blocks,
+                                                  num_ranks, interleave / block_size, rank,
+                                                  local_block_table, max_local_blocks,
+                                                  (hipStream_t)stream));
+}
+
+size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch, int32_t num_partitions) {
+  int32_t groups = 0;
+  if (check_desc(desc, &groups) != DCP_SUCCESS) return 0;
+  if (batch < 0 || batch > kMaxBatch || num_partitions < 0 || num_partitions > kMaxParts) return 0;
+  const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
+  return ws_layout(batch, parts, desc->num_q_heads, desc->v_dim).total;
+}
+
+dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_cache_blocks,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t batch, int32_t rank,
+                                int32_t num_ranks, int32_t interleave, int32_t num_partitions,
+                                void* workspace, size_t workspace_bytes, float* out_o,
+                                float* out_lse, void* stream) {
+  int32_t groups = 0;
+  dcp_status_t st = check_desc(desc, &groups);
+  if (st != DCP_SUCCESS) return st;
+  st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (batch < 0 || batch > kMaxBatch || num_partitions < 0 || num_partitions > kMaxParts ||
+      max_blocks_per_seq < 0 || num_cache_blocks < 0)
+    return DCP_ERROR_INVALID_VALUE;
+  if (batch == 0) return DCP_SUCCESS;
+  if (!q || !k_cache || !block_table || !seq_lens || !out_o || !out_lse) return DCP_ERROR_INVALID_VALUE;
+  if (num_cache_blocks < 1 || max_blocks_per_seq < 1) return DCP_ERROR_INVALID_VALUE;
+  if ((desc->kind == DCP_KV_MLA_LATENT) != (v_cache == nullptr)) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)out_o & 15) || ((uintptr_t)out_lse & 3)) return DCP_ERROR_INVALID_VALUE;
+  const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
+  const WsLayout wl = ws_layout(batch, parts, desc->num_q_heads, desc->v_dim);
+  if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < wl.total) return DCP_ERROR_WORKSPACE;
+
+  uint8_t* ws = (uint8_t*)workspace;
+  dcp::PartialParams p{};
+  p.q = (const uint16_t*)q;
+  p.k_cache = (const uint8_t*)k_cache;
+  p.v_cache = (const uint8_t*)v_cache;
+  p.num_cache_blocks = num_cache_blocks;
+  p.block_table = block_table;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.batch = batch;
+  p.num_q_heads = desc->num_q_heads;
+  p.num_kv_heads = desc->num_kv_heads;
+  p.block_size = desc->block_size;
+  p.num_head_groups = groups;
+  p.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+  p.part.seq_lens = seq_lens;
+  p.part.batch = batch;
+  p.part.rank = rank;
+  p.part.num_ranks = num_ranks;
+  p.part.interleave = interleave;
+  p.part.max_blocks_per_seq = max_blocks_per_seq;
+  p.part.block_size = desc->block_size;
+  p.part.tile = desc->kind == DCP_KV_MLA_LATENT ? dcp::kMlaTile : dcp::kGqaTile;
+  p.part.num_parts = parts;
+  p.out_o = out_o;
+  p.out_lse = out_lse;
+  p.ws_prefix = (int64_t*)(ws + wl.prefix);
+  p.ws_lse = (float*)(ws + wl.lse);
+  p.ws_o = (float*)(ws + wl.o);
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = desc->kind == DCP_KV_MLA_LATENT ? dcp::launch_mla_partial(p, s)
+                                                 : dcp::launch_gqa_partial(p, s);
+  if (e != hipSuccess) return DCP_ERROR_HIP;
+
+  dcp::SplitReduceParams r{};
+  r.ws_prefix = p.ws_prefix;
+  r.ws_lse = p.ws_lse;
+  r.ws_o = p.ws_o;
+  r.batch = batch;
+  r.num_heads = desc->num_q_heads;
+  r.v_dim = desc->v_dim;
+  r.num_parts = parts;
+  r.out_o = out_o;
+  r.out_lse = out_lse;
+  return hip_status(dcp::launch_split_reduce(r, s));
+}
+
+dcp_status_t dcp_merge(const float* o_parts, const float* lse_parts, int32_t num_parts,
+                       int32_t batch, int32_t num_heads, int32_t v_dim, float* out_o,
+                       float* out_lse, void* stream) {
+  if (num_parts < 1 || batch < 0 || num_heads < 0 || v_dim < 4 || v_dim % 4) return DCP_ERROR_INVALID_VALUE;
+  const int64_t rows = (int64_t)batch * num_heads;
+  if (rows == 0) return DCP_SUCCESS;
+  if (!o_parts || !lse_parts || !out_o) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)o_parts | (uintptr_t)out_o) & 15) return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_merge(o_parts, lse_parts, num_parts, rows, v_dim, out_o, out_lse,
+                                      (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Device-side helpers shared by the decode-attention kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dcp_params.h"
+#include "dcp_shard.h"
+
+#define DCP_LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((__vector_size__(8)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+namespace dcp {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Work-group barrier without a memory fence: the kernels order their LDS traffic
+// with explicit s_waitcnt, so the fence __syncthreads() adds (which also drains
+// every outstanding global load) is not wanted.  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte asynchronous global -> LDS copy.  Lane i's 16 bytes land at
+// lds_wave_base + 16 * i (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void dma16(const void* gsrc, DCP_LDS void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_wave_base, 16, 0, 0);
+}
+
+// LDS transpose read of four 16-bit values.  Inside each group of 16 lanes, lane
+// i receives element (i % 4) of the 8-byte pieces addressed by lanes
+// (i / 4) + 4e, e = 0..3.  If source lane s of the group addresses row r0 + s/4,
+// columns c0 + 4(s%4) .. +3 of a row-major bf16 matrix, lane i obtains column
+// c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const DCP_LDS void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((DCP_LDS i16x4*)p));
+}
+
+// Joins two transposed 4-element reads into one 8-element MFMA operand.  The
+// values are moved as whole dwords: assembling the bf16 vector element by element
+// from the 16-bit lanes of the read result is mis-packed by this compiler (it
+// duplicates element 0).
+__device__ __forceinline__ bf16x8 join_tr16(u32x2 lo, u32x2 hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Load through the constant address space: the data is read-only for the whole
+// kernel, so a wave-uniform address becomes a scalar load (counted by lgkmcnt, not
+// by vmcnt, so it never waits behind the in-flight direct-to-LDS tile copies).
+template <class T>
+__device__ __forceinline__ T ld_const(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+// ------------------------------------------------------------------ work partitions
+//
+// A rank's local tokens of the whole batch are cut into tiles of T tokens (a tile
+// never crosses a request), and the concatenated tile sequence into P equal spans:
+// span w covers tiles [floor(w*TT/P), floor((w+1)*TT/P)), TT being the total.  A
+// request whose tiles fall into several spans is computed piecewise; each piece
+// writes a partial (O, LSE) into a workspace slot and a second kernel merges them.
+// Span w owns slots 2w (its first request piece) and 2w+1 (its last).
+
+// Local length of request b actually processed (clamped to what its block table row holds).
+__device__ __forceinline__ int64_t part_local_len(const PartitionArgs& a, int b) {
+  int64_t L = ld_const(a.seq_lens + b);
+  int64_t lr = dcp_local_len(L < 0 ? 0 : L, a.num_ranks, a.interleave, a.rank);
+  const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
+  return lr < cap ? lr : cap;
+}
+
+__device__ __forceinline__ int64_t part_tiles(const PartitionArgs& a, int b) {
+  return (part_local_len(a, b) + a.tile - 1) / a.tile;
+}
+
+__device__ __forceinline__ int64_t span_start(int64_t w, int64_t TT, int64_t P) { return w * TT / P; }
+
+// The span that holds tile t (0 <= t < TT).
+__device__ __forceinline__ int64_t span_of(int64_t t, int64_t TT, int64_t P) {
+  return ((t + 1) * P - 1) / TT;
+}
+
+struct SpanLoc {
+  int64_t total;   // TT
+  int64_t start;   // first tile of the span
+  int64_t end;     // one past its last tile
+  int32_t b0;      // request of the first tile
+  int64_t off0;    // tile offset of the first tile inside request b0
+};
+
+// Block-cooperative: every thread of the block gets the location of span w.  If
+// prefix_out is non-null, the block also writes each request's first tile index
+// (prefix_out[b]) and the total (prefix_out[B]).  s_scan must hold blockDim.x
+// int64 values; s_loc two int64 values.
+template <int NT>
+__device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
+                               int64_t* s_scan, int64_t* s_loc) {
+  const int tid = threadIdx.x;
+  const int per = (a.batch + NT - 1) / NT;
+  const int b_lo = tid * per;
+  const int b_hi = min(a.batch, b_lo + per);
+  int64_t sum = 0;
+  for (int b = b_lo; b < b_hi; ++b) sum += part_tiles(a, b);
+  s_scan[tid] = sum;
+  if (tid == 0) { s_loc[0] = -1; s_loc[1] = 0; }
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the per-thread sums.
+  for (int d = 1; d < NT; d <<= 1) {
+    int64_t v = tid >= d ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  const int64_t incl = s_scan[tid];
+  const int64_t excl = incl - sum;
+  SpanLoc loc;
+  loc.total = s_scan[NT - 1];
+  loc.start = span_start(w, loc.total, a.num_parts);
+  loc.end = span_start(w + 1, loc.total, a.num_parts);
+  if (prefix_out) {
+    int64_t acc = excl;
+    for (int b = b_lo; b < b_hi; ++b) { prefix_out[b] = acc; acc += part_tiles(a, b); }
+    if (tid == NT - 1) prefix_out[a.batch] = loc.total;
+  }
+  if (loc.start < loc.end && excl <= loc.start && loc.start < incl) {
+    int64_t acc = excl;
+    for (int b = b_lo; b < b_hi; ++b) {
+      const int64_t n = part_tiles(a, b);
+      if (loc.start < acc + n) { s_loc[0] = b; s_loc[1] = loc.start - acc; break; }
+      acc += n;
+    }
+  }
+  __syncthreads();
+  loc.b0 = (int32_t)s_loc[0];
+  loc.off0 = s_loc[1];
+  __syncthreads();  // s_loc / s_scan may be reused after this
+  return loc;
+}
+
+// Split the flat block index into (span, head group).  Consecutive dispatches go
+// round-robin over the 8 XCDs, so blocks x and x + 8 share an XCD; with several
+// head groups the groups of one span are placed 8 apart, so they read the same
+// pages through the same L2 at about the same time.
+__device__ __forceinline__ void block_to_span(int num_parts, int num_groups, int64_t* w, int* g) {
+  const int x = blockIdx.x;
+  if (num_groups == 1) { *w = x; *g = 0; return; }
+  if (num_parts % 8 == 0) {
+    const int xcd = x % 8, k = x / 8;
+    *w = (int64_t)(k / num_groups) * 8 + xcd;
+    *g = k % num_groups;
+  } else {
+    *w = x / num_groups;
+    *g = x % num_groups;
+  }
+}
+
+__device__ __forceinline__ int32_t clamp_page(int32_t page, int64_t num_blocks) {
+  return (page < 0 || (int64_t)page >= num_blocks) ? 0 : page;
+}
+
+}  // namespace dcp

@@ -1,0 +1,45 @@
+// Parameter blocks passed by value to the kernels (plain data, host and device).
+#pragma once
+#include <stdint.h>
+
+namespace dcp {
+
+// How a rank's tiles are cut into work partitions (see the partition helpers in
+// dcp_device.h).
+struct PartitionArgs {
+  const int32_t* seq_lens;  // [B] global lengths (device)
+  int32_t batch;
+  int32_t rank, num_ranks, interleave;
+  int32_t max_blocks_per_seq, block_size;
+  int32_t tile;             // tokens per tile
+  int32_t num_parts;        // P
+};
+
+struct PartialParams {
+  const uint16_t* q;        // [B, H, qk_dim] bf16
+  const uint8_t* k_cache;   // page pool (bytes)
+  const uint8_t* v_cache;   // GQA V page pool (bytes); MLA: unused
+  int64_t num_cache_blocks;
+  const int32_t* block_table;
+  int32_t max_blocks_per_seq;
+  int32_t batch, num_q_heads, num_kv_heads, block_size;
+  int32_t num_head_groups;  // work-groups sharing one span (disjoint head sets)
+  float scale_log2;         // softmax_scale * log2(e)
+  PartitionArgs part;
+  float* out_o;             // [B, H, v_dim]
+  float* out_lse;           // [B, H]
+  int64_t* ws_prefix;       // [B + 1]
+  float* ws_lse;            // [2P, H]
+  float* ws_o;              // [2P, H, v_dim]
+};
+
+struct SplitReduceParams {
+  const int64_t* ws_prefix;  // [B + 1] first tile of each request, total at [B]
+  const float* ws_lse;       // [2P, H]
+  const float* ws_o;         // [2P, H, v_dim]
+  int32_t batch, num_heads, v_dim, num_parts;
+  float* out_o;              // [B, H, v_dim]
+  float* out_lse;            // [B, H]
+};
+
+}  // namespace dcp

@@ -1,0 +1,163 @@
+// Log-sum-exp merges and shard-map kernels.
+//
+// The merge rule is the one the vLLM blog "Efficient Decode Context Parallelism
+// with vLLM for Long Context Workloads" states in Sec. 4.1 ("AllGather +
+// ReduceScatter"): partial outputs over disjoint token sets are reweighted by
+// their LSE values (the online-softmax trick) and summed,
+//   LSE = ln sum_i exp(LSE_i),   O = sum_i exp(LSE_i - LSE) O_i.
+// It serves twice: inside a rank, to join the pieces of a request that several
+// work partitions computed (split-K), and across the N ranks.
+#include "dcp_device.h"
+#include "dcp_internal.h"
+
+namespace dcp {
+
+// ------------------------------------------------------------------ split-K reduce
+// One block of 256 threads per (request, group of heads); each thread owns 4
+// consecutive floats of one head's v_dim outputs (DV/4 threads per head).
+template <int DV>
+__global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceParams p) {
+  constexpr int kTph = DV / 4;         // threads per head
+  constexpr int kHpb = 256 / kTph;     // heads per block
+  static_assert(256 % kTph == 0, "head rows must tile the block");
+  const int b = blockIdx.x;
+  const int head = blockIdx.y * kHpb + (int)threadIdx.x / kTph;
+  const int t = threadIdx.x % kTph;
+  const int H = p.num_heads;
+  if (head >= H) return;
+
+  const int64_t F = p.ws_prefix[b];
+  const int64_t n = p.ws_prefix[b + 1] - F;
+  float* orow = p.out_o + ((int64_t)b * H + head) * DV + 4 * t;
+  if (n == 0) {
+    *(f32x4*)orow = f32x4{};
+    if (t == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
+    return;
+  }
+  const int64_t TT = p.ws_prefix[p.batch];
+  const int64_t P = p.num_parts;
+  const int64_t w_lo = span_of(F, TT, P);
+  const int64_t w_hi = span_of(F + n - 1, TT, P);
+  if (w_lo == w_hi) return;  // computed in one piece by the partial kernel
+
+  float mx = -INFINITY;
+  for (int64_t w = w_lo; w <= w_hi; ++w) {
+    const int64_t s0 = span_start(w, TT, P);
+    if (s0 == span_start(w + 1, TT, P)) continue;  // empty span
+    const int64_t slot = 2 * w + (s0 < F ? 1 : 0);
+    mx = fmaxf(mx, p.ws_lse[slot * H + head]);
+  }
+  f32x4 acc = f32x4{};
+  float wsum = 0.f;
+  for (int64_t w = w_lo; w <= w_hi; ++w) {
+    const int64_t s0 = span_start(w, TT, P);
+    if (s0 == span_start(w + 1, TT, P)) continue;
+    const int64_t slot = 2 * w + (s0 < F ? 1 : 0);
+    const float wt = fast_exp2((p.ws_lse[slot * H + head] - mx) * kLog2e);
+    wsum += wt;
+    acc += wt * *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * t);
+  }
+  *(f32x4*)orow = acc * (1.0f / wsum);
+  if (t == 0) p.out_lse[(int64_t)b * H + head] = mx + fast_log2(wsum) * kLn2;
+}
+
+hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream) {
+  if (p.batch == 0) return hipSuccess;
+  const int hpb = 256 / (p.v_dim / 4);
+  dim3 grid(p.batch, (p.num_heads + hpb - 1) / hpb);
+  if (p.v_dim == 512)
+    hipLaunchKernelGGL(split_reduce_kernel<512>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ N-way merge
+// One thread per 4 consecutive output floats of one (request, head) row; the row's
+// N LSE values are read by each of its threads (they stay in L1/L2).
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts,
+                                                    const float* __restrict__ lse_parts,
+                                                    int32_t num_parts, int64_t rows, int32_t v_dim,
+                                                    float* __restrict__ out_o,
+                                                    float* __restrict__ out_lse) {
+  const int quads = v_dim >> 2;
+  const int64_t total = rows * quads;
+  const int64_t part_stride = rows * v_dim;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = e / quads;
+    const int qd = (int)(e - row * quads);
+    float mx = -INFINITY;
+    for (int r = 0; r < num_parts; ++r) mx = fmaxf(mx, lse_parts[(int64_t)r * rows + row]);
+    f32x4 acc = f32x4{};
+    float wsum = 0.f;
+    if (mx != -INFINITY) {
+      for (int r = 0; r < num_parts; ++r) {
+        const float l = lse_parts[(int64_t)r * rows + row];
+        const float wt = fast_exp2((l - mx) * kLog2e);   // -inf -> 0
+        wsum += wt;
+        const f32x4 v = *(const f32x4*)(o_parts + r * part_stride + row * v_dim + 4 * qd);
+        if (wt != 0.f) acc += wt * v;
+      }
+      acc *= 1.0f / wsum;
+    }
+    *(f32x4*)(out_o + row * v_dim + 4 * qd) = acc;
+    if (qd == 0 && out_lse) out_lse[row] = mx == -INFINITY ? -INFINITY : mx + fast_log2(wsum) * kLn2;
+  }
+}
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int64_t rows,
+                        int32_t v_dim, float* out_o, float* out_lse, hipStream_t stream) {
+  const int64_t total = rows * (v_dim / 4);
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 1 << 20) blocks = 1 << 20;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, o_parts, lse_parts,
+                     num_parts, rows, v_dim, out_o, out_lse);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ shard map kernels
+__global__ void shard_map_kernel(const int32_t* __restrict__ seq_lens, int32_t batch, int32_t N,
+                                 int32_t I, int32_t rank, int32_t* __restrict__ local_lens) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= batch) return;
+  const int32_t L = seq_lens[b];
+  local_lens[b] = (int32_t)dcp_local_len(L < 0 ? 0 : L, N, I, rank);
+}
+
+hipError_t launch_shard_map(const int32_t* seq_lens, int32_t batch, int32_t N, int32_t I,
+                            int32_t rank, int32_t* local_lens, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(shard_map_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens,
+                     batch, N, I, rank, local_lens);
+  return hipGetLastError();
+}
+
+// Local page k of rank r = global page ((k / P) * N + r) * P + k % P, P = I / block_size.
+__global__ void local_block_table_kernel(const int32_t* __restrict__ gbt, int32_t batch,
+                                         int32_t max_global, int32_t N, int32_t P, int32_t rank,
+                                         int32_t* __restrict__ lbt, int32_t max_local) {
+  const int64_t total = (int64_t)batch * max_local;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = e / max_local;
+    const int64_t k = e - b * max_local;
+    const int64_t gk = ((k / P) * N + rank) * P + k % P;
+    lbt[e] = gk < max_global ? gbt[b * max_global + gk] : -1;
+  }
+}
+
+hipError_t launch_local_block_table(const int32_t* gbt, int32_t batch, int32_t max_global, int32_t N,
+                                    int32_t P, int32_t rank, int32_t* lbt, int32_t max_local,
+                                    hipStream_t stream) {
+  const int64_t total = (int64_t)batch * max_local;
+  if (total == 0) return hipSuccess;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(local_block_table_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, gbt, batch,
+                     max_global, N, P, rank, lbt, max_local);
+  return hipGetLastError();
+}
+
+}  // namespace dcp

@@ -1,0 +1,199 @@
+/*
+ * dcp.h — C ABI of libdcp: single-token decode attention over one rank's
+ * sequence-dimension shard of a paged KV cache, and the log-sum-exp merge that
+ * turns the shards' partial results into the full-context result.
+ *
+ * The operation is Decode Context Parallelism as the vLLM blog "Efficient Decode
+ * Context Parallelism with vLLM for Long Context Workloads" describes it:
+ *   - Sec. 4 ("What is DCP?"): the KV cache of every request is split along the
+ *     sequence dimension; each GPU holds and reads the cache of a subset of the
+ *     token positions (Sec. 2.2: 1/N of every request's KV).
+ *   - Sec. 4.1 ("Decode Context Parallelism Process"), "Compute": each GPU attends
+ *     the full single-token query against its local KV slice and produces a
+ *     partial output plus a log-sum-exp (LSE) per head; then the LSE values
+ *     reweight and merge the partials (the online-softmax trick) into the true
+ *     output.
+ *   - Sec. 5.3 (MLA backend): one latent KV vector shared by every query head;
+ *     Sec. 5.4 (GQA backend): each KV head is shared by a group of query heads.
+ *   - The vLLM-Ascend "Decode Context Parallel Guide", Constraints: the KV cache
+ *     interleave size (cp_kv_cache_interleave_size) and the page (block) size.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Sharding.   Global token position t of a request belongs to rank
+ *               (t / I) % N for interleave size I >= 1 and N >= 1 ranks.  A rank
+ *               stores its tokens densely in ascending global order: local index
+ *               j = (t / (N*I)) * I + t % I.  A request of global length L holds
+ *               L_r = (L / (N*I)) * I + clamp(L % (N*I) - r*I, 0, I) tokens on rank r.
+ *   Ownership.  The caller allocates every buffer.  The library allocates no
+ *               memory, keeps no pointer after a call returns and has no mutable
+ *               global state; calls are re-entrant.
+ *   Memory.     "device" pointers are HIP device memory of the current device;
+ *               "host" pointers are ordinary host memory.  Tensors are dense,
+ *               row-major, with the shapes given.
+ *   Streams.    `stream` is a hipStream_t (NULL = the default stream).  Device
+ *               work is enqueued on it; no call synchronises the device.
+ *   Errors.     Arguments the host can check are validated before anything is
+ *               enqueued; on failure a status other than DCP_SUCCESS is returned
+ *               and nothing runs.  DCP_ERROR_HIP reports a failed launch.
+ *               Device-resident values the host cannot see (page ids, lengths)
+ *               are clamped by the kernels so that no access leaves its buffer:
+ *               out-of-range page ids are replaced by page 0, negative lengths read
+ *               as 0, and a rank never reads more than max_blocks_per_seq pages of
+ *               a request.  Such inputs give meaningless numbers, never a fault.
+ */
+#ifndef DCP_H_
+#define DCP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DCP_SUCCESS = 0,
+  DCP_ERROR_INVALID_VALUE = 1, /* a null pointer, a size or an index out of range */
+  DCP_ERROR_NOT_SUPPORTED = 2, /* a valid shape this build has no kernel for */
+  DCP_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  DCP_ERROR_HIP = 4            /* the HIP runtime reported an error */
+} dcp_status_t;
+
+typedef enum {
+  /* MLA (blog Sec. 5.3): one latent KV head; the cache row is the latent vector
+   * (qk_dim = 576 = 512 latent + 64 rope); K is the whole row and V its first
+   * v_dim (= 512) entries.  The query is in the same latent space. */
+  DCP_KV_MLA_LATENT = 0,
+  /* GQA (blog Sec. 5.4): num_kv_heads KV heads; query head h reads KV head
+   * h / (num_q_heads / num_kv_heads).  K and V live in separate caches. */
+  DCP_KV_GQA = 1
+} dcp_kv_kind_t;
+
+typedef struct {
+  int32_t kind;          /* dcp_kv_kind_t */
+  int32_t num_q_heads;   /* H */
+  int32_t num_kv_heads;  /* 1 for MLA; H % num_kv_heads == 0 for GQA */
+  int32_t qk_dim;        /* 576 for MLA, 128 for GQA */
+  int32_t v_dim;         /* 512 for MLA, 128 for GQA */
+  int32_t block_size;    /* tokens per KV page */
+  float softmax_scale;   /* logits are softmax_scale * (q . k), applied in fp32 */
+} dcp_attn_desc_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* dcp_status_string(int32_t status);
+
+/* ------------------------------------------------------------------ shard map
+ * Blog Sec. 4 and Sec. 2.2; interleave size from the vLLM-Ascend guide.     */
+
+/* Local lengths of one rank (host).
+ *   seq_lens   host int32 [batch]: global request lengths (including the
+ *              current decode token); must be >= 0.
+ *   local_lens host int32 [batch], written: L_r of every request.
+ *   total_local, max_local: optional (NULL allowed) host outputs, the sum and
+ *              the maximum of local_lens.
+ * Errors: INVALID_VALUE if batch < 0, num_ranks < 1, interleave < 1,
+ * rank not in [0, num_ranks), a needed pointer is NULL, or a length < 0.   */
+dcp_status_t dcp_shard_map(const int32_t* seq_lens, int32_t batch, int32_t num_ranks,
+                           int32_t interleave, int32_t rank, int32_t* local_lens,
+                           int64_t* total_local, int32_t* max_local);
+
+/* Owner rank and local index of global positions (host).
+ *   positions host int64 [count] (>= 0); owner host int32 [count] and
+ *   local_index host int64 [count] are written.                              */
+dcp_status_t dcp_shard_locate(const int64_t* positions, int64_t count, int32_t num_ranks,
+                              int32_t interleave, int32_t* owner, int64_t* local_index);
+
+/* Global position of rank-local indices (host): the inverse of dcp_shard_locate.
+ *   local_index host int64 [count] (>= 0); positions host int64 [count] written. */
+dcp_status_t dcp_shard_global(const int64_t* local_index, int64_t count, int32_t num_ranks,
+                              int32_t interleave, int32_t rank, int64_t* positions);
+
+/* Local lengths of one rank computed on the device with the same code the
+ * attention kernels use.  seq_lens, local_lens: device int32 [batch].         */
+dcp_status_t dcp_shard_map_device(const int32_t* seq_lens, int32_t batch, int32_t num_ranks,
+                                  int32_t interleave, int32_t rank, int32_t* local_lens,
+                                  void* stream);
+
+/* A rank's block table viewed out of a request-global block table (device),
+ * for page-aligned interleaving: requires interleave % block_size == 0, so each
+ * global page lies wholly on one rank.  With P = interleave / block_size, local
+ * page k of rank r is global page ((k / P) * N + r) * P + k % P.
+ *   global_block_table device int32 [batch, max_global_blocks]
+ *   local_block_table  device int32 [batch, max_local_blocks], written; entries
+ *                      whose global page falls outside the table are set to -1.
+ * Errors: INVALID_VALUE for bad sizes/rank/pointers; NOT_SUPPORTED if
+ * interleave % block_size != 0.                                               */
+dcp_status_t dcp_local_block_table(const int32_t* global_block_table, int32_t batch,
+                                   int32_t max_global_blocks, int32_t num_ranks,
+                                   int32_t interleave, int32_t block_size, int32_t rank,
+                                   int32_t* local_block_table, int32_t max_local_blocks,
+                                   void* stream);
+
+/* ------------------------------------------------------------------ partial attention
+ * Blog Sec. 4.1 "Compute", Sec. 5.3 (MLA), Sec. 5.4 (GQA).                 */
+
+/* Workspace bytes dcp_decode_partial needs for `batch` requests split into
+ * `num_partitions` token-balanced work partitions (0 = the library's default
+ * for the current device).  Returns 0 for an invalid or unsupported desc.     */
+size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
+                                 int32_t num_partitions);
+
+/* One rank's partial decode attention.
+ *   q            device bf16 [batch, H, qk_dim]: the full (gathered) query.
+ *   k_cache      device bf16, this rank's page pool:
+ *                  MLA: [num_cache_blocks, block_size, qk_dim] latent rows;
+ *                  GQA: [num_cache_blocks, block_size, num_kv_heads, qk_dim].
+ *   v_cache      MLA: must be NULL (V is the first v_dim entries of each latent
+ *                row); GQA: device bf16 [num_cache_blocks, block_size,
+ *                num_kv_heads, v_dim].
+ *   block_table  device int32 [batch, max_blocks_per_seq]: entry k of request b
+ *                is the pool page holding the rank's local tokens
+ *                [k*block_size, (k+1)*block_size) of that request.
+ *   seq_lens     device int32 [batch]: GLOBAL lengths; the kernel derives each
+ *                request's local length from (seq_lens, rank, num_ranks,
+ *                interleave).
+ *   num_partitions  work partitions per head group (0 = default).  The rank's
+ *                local tokens are cut into this many equal token ranges across
+ *                the batch; a request cut between partitions is reduced in a
+ *                second kernel (split-K).
+ *   workspace    device, >= dcp_decode_workspace_size(desc, batch, num_partitions)
+ *                bytes, 256-byte aligned; contents need no initialisation.
+ *   out_o        device fp32 [batch, H, v_dim], written: normalised partial output
+ *                O_r = sum_t p_t v_t / sum_t p_t over the rank's tokens.
+ *   out_lse      device fp32 [batch, H], written: LSE_r = ln sum_t exp(s_t),
+ *                s_t = softmax_scale * (q . k_t).
+ *   A request with no local tokens gets O_r = 0 and LSE_r = -inf.
+ * Supported: MLA with qk_dim 576, v_dim 512, 1 <= H <= 128, block_size a
+ * multiple of 32; GQA with qk_dim = v_dim = 128, H / num_kv_heads <= 16,
+ * block_size a multiple of 16 or 16 a multiple of block_size.
+ * Errors: INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP (nothing runs on error). */
+dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_cache_blocks,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t batch, int32_t rank,
+                                int32_t num_ranks, int32_t interleave, int32_t num_partitions,
+                                void* workspace, size_t workspace_bytes, float* out_o,
+                                float* out_lse, void* stream);
+
+/* ------------------------------------------------------------------ merge
+ * Blog Sec. 4.1, "AllGather + ReduceScatter": the LSE values reweight and merge
+ * the partials.  LSE = ln sum_r exp(LSE_r);  O = sum_r exp(LSE_r - LSE) O_r.
+ * Parts with LSE_r = -inf carry no weight; if all are -inf, O = 0, LSE = -inf. */
+
+/* N-way merge of num_parts partial results.
+ *   o_parts   device fp32 [num_parts, batch, H, v_dim]
+ *   lse_parts device fp32 [num_parts, batch, H]
+ *   out_o     device fp32 [batch, H, v_dim], written (must not alias the inputs)
+ *   out_lse   device fp32 [batch, H], written (nullable: LSE not stored).
+ * Errors: INVALID_VALUE for num_parts < 1, negative sizes, v_dim not a
+ * multiple of 4 or NULL inputs.                                              */
+dcp_status_t dcp_merge(const float* o_parts, const float* lse_parts, int32_t num_parts,
+                       int32_t batch, int32_t num_heads, int32_t v_dim, float* out_o,
+                       float* out_lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCP_H_ */

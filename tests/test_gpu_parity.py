@@ -1,0 +1,337 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances (bf16 inputs, fp32 accumulation): max |dO| <= 5e-3, max |dLSE| <= 1e-3.
+Shard assignment is checked bit-exactly (device shard map, census counts).
+Inputs are regenerated on both sides from the same seeds; the oracle never sees
+a value produced by the library.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dcp_inputs as di
+import decode_attention_sequence_paged_amd as dcp
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = 5e-3
+TOL_LSE = 1e-3
+
+
+def _paged():
+    from dcp_inputs import paged
+    return paged
+
+
+def _wl(name, **kw):
+    base = di.WORKLOADS[name]
+    d = dict(base.__dict__)
+    d.update(kw)
+    return di.Workload(**d)
+
+
+def run_rank(wl, rank, census=False, parts=0, q=None, lengths=None):
+    pg = _paged()
+    lengths = wl.lengths if lengths is None else lengths
+    rc = pg.build_rank_cache(wl, rank, census=census, lengths=np.asarray(lengths))
+    if q is None:
+        q = pg.device_query(wl, census=census)
+    sl = torch.tensor(np.asarray(lengths, dtype=np.int32), device="cuda")
+    o = torch.full((wl.batch, wl.num_q_heads, wl.v_dim), float("nan"), device="cuda")
+    lse = torch.full((wl.batch, wl.num_q_heads), float("nan"), device="cuda")
+    ws = pg.workspace_for(wl, parts)
+    pg.run_partial(wl, rc, q, sl, o, lse, ws, num_partitions=parts)
+    torch.cuda.synchronize()
+    return o, lse, rc
+
+
+def check_close(o_gpu, lse_gpu, o_ref, lse_ref, what):
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse_gpu), empty), what + ": empty-set pattern differs"
+    if empty.any():
+        assert np.all(o_gpu[empty] == 0.0), what + ": empty set must give O = 0"
+    full = ~empty
+    if full.any():
+        do = np.abs(o_gpu[full] - o_ref[full]).max()
+        dl = np.abs(lse_gpu[full] - lse_ref[full]).max()
+        print("%s: max|dO|=%.3g max|dLSE|=%.3g" % (what, do, dl), flush=True)
+        assert np.all(np.isfinite(o_gpu[full])), what + ": non-finite O"
+        assert do <= TOL_O, "%s: max|dO| = %g" % (what, do)
+        assert dl <= TOL_LSE, "%s: max|dLSE| = %g" % (what, dl)
+
+
+def oracle_rank(wl, b, rank, lengths=None, census=False):
+    L = int((wl.lengths if lengths is None else lengths)[b])
+    toks = oracle.rank_tokens(L, wl.dcp_size, wl.interleave, rank)
+    return oracle_tokens(wl, b, toks, census)
+
+
+def oracle_tokens(wl, b, toks, census=False):
+    if census:
+        H = wl.num_q_heads
+        q = np.zeros((H, wl.qk_dim))
+        rows = di.bf16_bits_to_f64(di.census_rows_numpy(toks, wl.qk_dim))
+        K = np.repeat(rows[:, None, :], wl.num_kv_heads, axis=1)
+        return oracle.attention(q, K, K[..., :wl.v_dim], wl.softmax_scale)
+    q, K, V = oracle.request_inputs(wl, b, toks)
+    return oracle.attention(q, K, V, wl.softmax_scale)
+
+
+# ----------------------------------------------------------------------------- building blocks
+
+def test_device_generator_matches_host():
+    rows = torch.from_numpy(np.random.default_rng(3).integers(0, 2 ** 40, 3000)).cuda()
+    dst = torch.arange(3000, dtype=torch.int64, device="cuda")
+    for cols, stream, mode in [(576, 1, 0), (128, 2, 0), (576, 1, 1)]:
+        buf = torch.empty((3000, cols), dtype=torch.int16, device="cuda")
+        di.device_fill_rows(buf, dst, rows, cols, 7, stream, mode=mode)
+        torch.cuda.synchronize()
+        host = di.host_rows(rows.cpu().numpy().astype(np.uint64), cols, 7, stream, mode=mode)
+        assert np.array_equal(buf.cpu().numpy().view(np.uint16), host)
+
+
+@pytest.mark.parametrize("N,I", [(1, 1), (2, 1), (4, 1), (8, 128), (3, 5), (7, 1000)])
+def test_device_shard_map_bitexact(N, I):
+    L = np.concatenate([np.arange(0, 300), np.array([1 << 20, 999999, 65536, 65535, 200000])])
+    sl = torch.tensor(L.astype(np.int32), device="cuda")
+    out = torch.empty_like(sl)
+    for r in range(N):
+        dcp.dcp_shard_map_device(sl, N, I, r, out)
+        torch.cuda.synchronize()
+        ref = np.array([oracle.rank_length(int(x), N, I, r) for x in L])
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
+def test_local_block_table_view():
+    N, I, bs = 4, 256, 128
+    B, MG = 3, 40
+    g = torch.from_numpy(np.random.default_rng(5).integers(0, 10 ** 6, (B, MG)).astype(np.int32)).cuda()
+    for r in range(N):
+        ml = 12
+        loc = torch.empty((B, ml), dtype=torch.int32, device="cuda")
+        dcp.dcp_local_block_table(g, N, I, bs, r, loc)
+        torch.cuda.synchronize()
+        toks = oracle.rank_tokens(MG * bs + N * I, N, I, r)   # enough positions
+        gl = g.cpu().numpy()
+        for k in range(ml):
+            t = int(toks[k * bs])                              # first token of local page k
+            ref = gl[:, t // bs] if t // bs < MG else np.full(B, -1)
+            assert np.array_equal(loc.cpu().numpy()[:, k], ref)
+
+
+def test_merge_kernel_against_oracle():
+    rng = np.random.default_rng(8)
+    for (N, B, H, Dv) in [(8, 3, 16, 512), (4, 5, 64, 128), (1, 2, 4, 512), (3, 1, 2, 4)]:
+        O = rng.standard_normal((N, B, H, Dv)).astype(np.float32)
+        L = (rng.standard_normal((N, B, H)) * 20).astype(np.float32)
+        L[rng.random((N, B, H)) < 0.3] = -np.inf
+        if N > 1:
+            L[:, 0, 0] = -np.inf                               # an all-empty row
+        empty = np.isneginf(L)
+        O_or = O.copy(); O_or[empty] = 0.0
+        O_gpu = O.copy(); O_gpu[empty] = np.nan                # empty parts must carry no weight
+        o_ref, l_ref = oracle.merge(O_or.astype(np.float64), L.astype(np.float64))
+        og = torch.empty((B, H, Dv), device="cuda")
+        lg = torch.empty((B, H), device="cuda")
+        dcp.dcp_merge(torch.from_numpy(O_gpu).cuda(), torch.from_numpy(L).cuda(), og, lg)
+        torch.cuda.synchronize()
+        og, lg = og.cpu().numpy(), lg.cpu().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(l_ref))
+        fin = np.isfinite(l_ref)
+        assert np.allclose(og[fin], o_ref[fin], rtol=1e-5, atol=1e-5)
+        assert np.allclose(lg[fin], l_ref[fin], rtol=1e-6, atol=1e-5)
+        assert np.all(og[~fin] == 0)
+
+
+# ----------------------------------------------------------------------------- configurations
+
+@pytest.mark.parametrize("parts", [0, 1, 5, 64])
+def test_mla_tiny_every_rank_and_merge(parts):
+    """B=2, 16 heads, seq_lens {1000, 3000}, block size 64, N=2, I=1."""
+    wl = di.WORKLOADS["mla_tiny"]
+    o_parts, l_parts = [], []
+    for r in range(wl.dcp_size):
+        o, lse, _ = run_rank(wl, r, parts=parts)
+        o_parts.append(o)
+        l_parts.append(lse)
+        for b in range(wl.batch):
+            Or, Lr = oracle_rank(wl, b, r)
+            check_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), Or, Lr, "mla_tiny r%d b%d" % (r, b))
+    om = torch.empty_like(o_parts[0])
+    lm = torch.empty_like(l_parts[0])
+    dcp.dcp_merge(torch.stack(o_parts), torch.stack(l_parts), om, lm)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        Of, Lf = oracle.full_attention(wl, b)
+        check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Of, Lf, "mla_tiny merged b%d" % b)
+
+
+def _census_check(wl, parts=0, lengths=None, ranks=None):
+    """q = 0 and V rows = bits of the global token id: O * L_r recovers, exactly, how many
+    attended tokens have each bit set, so a dropped or duplicated token fails."""
+    lengths = wl.lengths if lengths is None else lengths
+    for r in (range(wl.dcp_size) if ranks is None else ranks):
+        o, lse, rc = run_rank(wl, r, census=True, parts=parts, lengths=lengths)
+        o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+        for b in range(len(lengths)):
+            toks = oracle.rank_tokens(int(lengths[b]), wl.dcp_size, wl.interleave, r)
+            if toks.size == 0:
+                assert np.all(np.isneginf(lse[b])) and np.all(o[b] == 0)
+                continue
+            counts = np.array([((toks >> d) & 1).sum() for d in range(24)], dtype=np.float64)
+            got = np.rint(o[b][:, :24] * toks.size)
+            assert np.array_equal(got, np.broadcast_to(counts, got.shape)), (r, b)
+            assert np.all(o[b][:, 24:] == 0)
+            assert np.allclose(lse[b], math.log(toks.size), atol=1e-4)
+
+
+@pytest.mark.parametrize("parts", [0, 3])
+def test_mla_tiny_census(parts):
+    _census_check(di.WORKLOADS["mla_tiny"], parts=parts)
+
+
+def test_gqa_b32_every_rank_and_merge():
+    """B=32, 64 query heads, 4 KV heads, head_dim 128, block 16, lengths U[4k,32k], N=4, I=1."""
+    wl = di.WORKLOADS["gqa_b32"]
+    o_parts, l_parts = [], []
+    sample = [0, 5, 12, 31]
+    for r in range(wl.dcp_size):
+        o, lse, _ = run_rank(wl, r)
+        o_parts.append(o)
+        l_parts.append(lse)
+        for b in (sample if r else range(wl.batch)):
+            Or, Lr = oracle_rank(wl, b, r)
+            check_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), Or, Lr, "gqa r%d b%d" % (r, b))
+    om = torch.empty_like(o_parts[0])
+    lm = torch.empty_like(l_parts[0])
+    dcp.dcp_merge(torch.stack(o_parts), torch.stack(l_parts), om, lm)
+    torch.cuda.synchronize()
+    for b in sample:
+        Of, Lf = oracle.full_attention(wl, b)
+        check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Of, Lf, "gqa merged b%d" % b)
+
+
+def test_gqa_census():
+    wl = _wl("gqa_b32", batch=4, lengths=(4096, 77, 1, 20001))
+    _census_check(wl)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+EDGE_LENGTHS = (0, 1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 257, 1000, 4099)
+
+
+@pytest.mark.parametrize("H,N,I,bs", [(16, 3, 5, 32), (64, 8, 128, 128), (40, 2, 1, 64),
+                                      (128, 4, 16, 64), (1, 1, 1, 32), (96, 5, 7, 96)])
+def test_mla_edge_lengths(H, N, I, bs):
+    wl = di.Workload("mla_edge", "mla", len(EDGE_LENGTHS), H, 1, 576, 512, bs, N, I, 21, EDGE_LENGTHS)
+    for r in sorted({0, N - 1}):
+        for parts in (0, 7):
+            o, lse, _ = run_rank(wl, r, parts=parts)
+            for b in range(wl.batch):
+                Or, Lr = oracle_rank(wl, b, r)
+                check_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), Or, Lr,
+                            "mla_edge H%d r%d p%d b%d" % (H, r, parts, b))
+
+
+@pytest.mark.parametrize("H,Hkv,N,I,bs", [(64, 4, 4, 1, 16), (32, 8, 2, 3, 32), (8, 1, 3, 16, 16),
+                                          (16, 2, 1, 1, 48), (48, 4, 5, 64, 64)])
+def test_gqa_edge_lengths(H, Hkv, N, I, bs):
+    wl = di.Workload("gqa_edge", "gqa", len(EDGE_LENGTHS), H, Hkv, 128, 128, bs, N, I, 22, EDGE_LENGTHS)
+    for r in sorted({0, N - 1}):
+        for parts in (0, 5):
+            o, lse, _ = run_rank(wl, r, parts=parts)
+            for b in range(wl.batch):
+                Or, Lr = oracle_rank(wl, b, r)
+                check_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), Or, Lr,
+                            "gqa_edge H%d/%d r%d p%d b%d" % (H, Hkv, r, parts, b))
+
+
+def test_mla_census_edge():
+    wl = di.Workload("mla_edge", "mla", len(EDGE_LENGTHS), 64, 1, 576, 512, 64, 3, 5, 23, EDGE_LENGTHS)
+    _census_check(wl, parts=11)
+    _census_check(wl, parts=0)
+
+
+def test_peaky_logits():
+    """Query scaled x8: near one-hot softmax rows, large logit range."""
+    wl = _wl("mla_tiny")
+    pg = _paged()
+    q = pg.device_query(wl) * 8                                  # exact in bf16
+    for r in range(wl.dcp_size):
+        o, lse, _ = run_rank(wl, r, q=q)
+        for b in range(wl.batch):
+            toks = oracle.rank_tokens(int(wl.lengths[b]), wl.dcp_size, wl.interleave, r)
+            qb, K, V = oracle.request_inputs(wl, b, toks)
+            Or, Lr = oracle.attention(qb * 8, K, V, wl.softmax_scale)
+            check_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), Or, Lr, "peaky r%d b%d" % (r, b))
+
+
+def test_merge_order_and_lost_rank_on_gpu():
+    """Merging ranks in any order gives the same result; merging N-1 ranks gives attention
+    over the union of their tokens (a defined degraded result)."""
+    wl = di.WORKLOADS["mla_tiny"]
+    parts = [run_rank(wl, r)[:2] for r in range(wl.dcp_size)]
+    o_all = torch.stack([p[0] for p in parts])
+    l_all = torch.stack([p[1] for p in parts])
+    res = []
+    for order in ([0, 1], [1, 0]):
+        om = torch.empty_like(parts[0][0]); lm = torch.empty_like(parts[0][1])
+        dcp.dcp_merge(o_all[order].contiguous(), l_all[order].contiguous(), om, lm)
+        res.append((om.cpu().numpy(), lm.cpu().numpy()))
+    assert np.allclose(res[0][0], res[1][0], atol=1e-6) and np.allclose(res[0][1], res[1][1], atol=1e-6)
+    om = torch.empty_like(parts[0][0]); lm = torch.empty_like(parts[0][1])
+    dcp.dcp_merge(o_all[1:].contiguous(), l_all[1:].contiguous(), om, lm)
+    for b in range(wl.batch):
+        Or, Lr = oracle_rank(wl, b, 1)
+        check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Or, Lr, "lost-rank b%d" % b)
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def _sample_requests(lengths, k=4):
+    L = np.asarray(lengths)
+    idx = {int(np.argmax(L)), int(np.argmin(L)), int(np.argsort(L)[len(L) // 2])}
+    rng = np.random.default_rng(99)
+    while len(idx) < min(k, len(L)):
+        idx.add(int(rng.integers(len(L))))
+    return sorted(idx)
+
+
+@pytest.mark.parametrize("name", ["mla_long_b128", "mla_c512", "mla_1m"])
+def test_full_size_mla(name):
+    """Full-size long-context MLA workloads in the launch configuration the benchmark
+    times (default partitions): rank 0 and rank N-1 partials and the N-way merge on
+    sampled requests (the longest, the shortest, the median, one more)."""
+    wl = di.WORKLOADS[name]
+    pg = _paged()
+    q = pg.device_query(wl)
+    sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+    ws = pg.workspace_for(wl)
+    o_all = torch.empty((wl.dcp_size, wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+    l_all = torch.empty((wl.dcp_size, wl.batch, wl.num_q_heads), device="cuda")
+    for r in range(wl.dcp_size):
+        rc = pg.build_rank_cache(wl, r)
+        pg.run_partial(wl, rc, q, sl, o_all[r], l_all[r], ws)
+        torch.cuda.synchronize()
+        del rc
+    om = torch.empty_like(o_all[0]); lm = torch.empty_like(l_all[0])
+    dcp.dcp_merge(o_all, l_all, om, lm)
+    torch.cuda.synchronize()
+    sample = _sample_requests(wl.lengths)
+    for b in sample:
+        for r in (0, wl.dcp_size - 1):
+            Or, Lr = oracle_rank(wl, b, r)
+            check_close(o_all[r, b].cpu().numpy(), l_all[r, b].cpu().numpy(), Or, Lr,
+                        "%s r%d b%d (L=%d)" % (name, r, b, wl.lengths[b]))
+        if wl.lengths[b] <= 300000:
+            Of, Lf = oracle.full_attention(wl, b)
+        else:  # merge of the oracle's own per-rank partials, for memory
+            pr = [oracle_rank(wl, b, r) for r in range(wl.dcp_size)]
+            Of, Lf = oracle.merge([p[0] for p in pr], [p[1] for p in pr])
+        check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Of, Lf, "%s merged b%d" % (name, b))
