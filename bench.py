@@ -1,0 +1,248 @@
+"""Benchmark of one decode-attention layer under Decode Context Parallelism on one GPU.
+
+A step is the whole hot path for one decode batch: the partial attention of every
+rank of the DCP group (ranks 0..N-1 run one after another on this GPU, each over
+its own sequence shard of the paged KV cache) followed by the N-way LSE merge.
+Inputs (query, every rank's page pool and block table) are resident in HBM
+before timing starts.
+
+Printed as one JSON line:
+  value            KV bytes of all ranks / step time (GB/s): whole-job throughput
+  ms_per_step      wall time of one step (K steps bracketed by synchronize)
+  rank0_kv_gbps    local-shard KV GB/s of rank 0's partial call (HIP events)
+  roofline         the partial-attention call against the 8 TB/s HBM peak
+  cpu_baseline     the float64 oracle on the host cores, per-rank partials of the batch
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "local-shard decode-attn KV GB/s & % of HBM peak; decode steps/s per batch"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_partial_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mla_long_b128")
+    ap.add_argument("--partitions", type=int, default=0, help="work partitions per head group (0 = default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle math to time for the CPU baseline")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("mla_partial.hip", "dcp_device.h"):
+        with open(os.path.join(ROOT, "decode_attention_sequence_paged_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float):
+    """Time the float64 oracle on the host: per-rank partial attention of the
+    workload's requests, rank 0 first, then rank 1, ... until about ``budget_s``
+    seconds of attention math have been timed (input regeneration is timed
+    separately and excluded)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    tokens = 0
+    t_math = t_gen = 0.0
+    done = []
+    for r in range(wl.dcp_size):
+        for b in range(wl.batch):
+            toks = oracle.rank_tokens(int(wl.lengths[b]), wl.dcp_size, wl.interleave, r)
+            t0 = time.perf_counter()
+            q, K, V = oracle.request_inputs(wl, b, toks)
+            t1 = time.perf_counter()
+            oracle.attention(q, K, V, wl.softmax_scale)
+            t2 = time.perf_counter()
+            t_gen += t1 - t0
+            t_math += t2 - t1
+            tokens += toks.size
+            del q, K, V
+        done.append(r)
+        if t_math >= budget_s:
+            break
+    kv_bytes = tokens * wl.qk_dim * 2
+    return {
+        "value": round(kv_bytes / t_math / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": "per-rank partial attention of all %d requests on ranks %s of %d (%d local tokens); "
+                  "%.3g s of float64 math timed, input regeneration (%.3g s) excluded; "
+                  "rate in bf16-KV bytes per second"
+                  % (wl.batch, ",".join(map(str, done)), wl.dcp_size, tokens, t_math, t_gen),
+        "tokens_per_s": round(tokens / t_math, 1),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the N ranks of the DCP group are emulated one after "
+              "another on a single device, so --gpus %d is not supported." % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dcp_inputs as di
+    import decode_attention_sequence_paged_amd as dcp
+    from dcp_inputs import paged
+
+    dcp.lib()
+    torch.cuda.set_device(0)
+    wl = di.WORKLOADS[args.workload]
+    N = wl.dcp_size
+
+    q = paged.device_query(wl)
+    sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+    ranks = [paged.build_rank_cache(wl, r) for r in range(N)]
+    ws = paged.workspace_for(wl, args.partitions)
+    o_all = torch.empty((N, wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+    l_all = torch.empty((N, wl.batch, wl.num_q_heads), device="cuda")
+    o = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+    lse = torch.empty((wl.batch, wl.num_q_heads), device="cuda")
+    torch.cuda.synchronize()
+
+    def step(evs=None):
+        for r in range(N):
+            if evs is not None:
+                evs[r][0].record()
+            paged.run_partial(wl, ranks[r], q, sl, o_all[r], l_all[r], ws, args.partitions)
+            if evs is not None:
+                evs[r][1].record()
+        if evs is not None:
+            evs[N][0].record()
+        dcp.dcp_merge(o_all, l_all, o, lse)
+        if evs is not None:
+            evs[N][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by synchronize
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-call durations with HIP events on the launch stream (separate pass)
+    per_call = np.zeros((args.steps, N + 1))
+    for s in range(args.steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(N + 1)]
+        step(evs)
+        torch.cuda.synchronize()
+        per_call[s] = [a.elapsed_time(b) for a, b in evs]
+    t_rank = per_call[:, :N].mean(axis=0)          # ms per rank call
+    t_merge = float(per_call[:, N].mean())
+
+    H, Dqk, Dv = wl.num_q_heads, wl.qk_dim, wl.v_dim
+    row_bytes = Dqk * 2
+    local = np.array([rc.total_local for rc in ranks], dtype=np.float64)
+    pages = np.array([int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum()) for rc in ranks])
+    kv_bytes = local * row_bytes
+    # compulsory bytes of one partial call: KV rows once, q, O_r, LSE_r, block-table entries
+    call_bytes = kv_bytes + wl.batch * H * (Dqk * 2 + Dv * 4 + 4) + pages * 4
+    merge_bytes = (N + 1) * wl.batch * H * (Dv + 1) * 4
+    flops_rank = 2.0 * H * (Dqk + Dv) * local
+
+    achieved = float(call_bytes.mean() / (t_rank.mean() * 1e-3) / 1e9)
+    rank0_kv = float(kv_bytes[0] / (t_rank[0] * 1e-3) / 1e9)
+    value = float(kv_bytes.sum() / (ms_per_step * 1e-3) / 1e9)
+    step_event_ms = float(t_rank.sum() + t_merge)
+    traffic = measured_traffic(float(call_bytes.mean()))
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: MLA decode, B=%d, %d query heads, 576-dim latent KV (V = first 512), "
+                        "pages of %d tokens, N=%d ranks, interleave I=%d, bimodal lengths "
+                        "(median %d, max %d), all N ranks' partials + N-way merge per step"
+                        % (wl.name, wl.batch, H, wl.block_size, N, wl.interleave,
+                           int(np.median(wl.lengths)), int(max(wl.lengths))),
+            "global_batch": wl.batch,
+            "seq_len": int(np.median(wl.lengths)),
+            "parallelism": "dcp%d emulated on 1 GPU" % N,
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "steps_per_s": round(1e3 / ms_per_step, 3),
+        "decode_tokens_per_s": round(wl.batch * 1e3 / ms_per_step, 1),
+        "steps_per_s_per_rank_equiv": round(1e3 / (t_rank[0] + t_merge / N), 3),
+        "rank0_kv_gbps": round(rank0_kv, 2),
+        "rank0_pct_hbm_peak": round(100.0 * rank0_kv / HBM_PEAK_GBPS, 2),
+        "rank0_local_kv_tokens_per_s": round(local[0] / (t_rank[0] * 1e-3), 1),
+        "rank_call_ms": [round(float(x), 4) for x in t_rank],
+        "merge_ms": round(t_merge, 4),
+        "merge_frac": round(t_merge / step_event_ms, 4),
+        "merge_gbps": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
+        "mfma_pct_bf16_peak": round(100.0 * float(flops_rank.mean() / (t_rank.mean() * 1e-3))
+                                    / (MFMA_BF16_PEAK_TFLOPS * 1e12), 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "dcp_decode_partial (mla_partial_kernel + split_reduce_kernel), mean over ranks",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": round(float(call_bytes.mean())),
+            "launch_ms": round(float(t_rank.mean()), 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
