@@ -13,8 +13,12 @@ SOURCES = ["dcp_api.hip", "mla_partial.hip", "gqa_partial.hip", "reduce.hip"]
 ARCH = os.environ.get("DCP_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are disabled: hipcc must not emit v_pk_{add,mul,fma}_f32.
+# MFMA accumulators are allocated in VGPRs (the "VGPR form"), which leaves the
+# accumulation registers to the MLA kernel's query slice and avoids copying the
+# O accumulator between register files every tile.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=" + ARCH,
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-mfma-vgpr-form",
                "-I", os.path.join(ROOT, "include")]
 
 

@@ -38,6 +38,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// The same wait as a compiler builtin, so the compiler's own wait-count tracking
+// sees it (it then knows every older load, e.g. of the query slice, has landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_builtin() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt immediate: vmcnt[3:0], expcnt[6:4] = 7 (no wait), lgkmcnt[11:8] = 15
+  // (no wait), vmcnt[5:4] in bits [15:14].
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
 // 16-byte asynchronous global -> LDS copy.  Lane i's 16 bytes land at
 // lds_wave_base + 16 * i (lds_wave_base must be wave-uniform).
 __device__ __forceinline__ void dma16(const void* gsrc, DCP_LDS void* lds_wave_base) {

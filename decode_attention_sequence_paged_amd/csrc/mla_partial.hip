@@ -7,23 +7,25 @@
 // the latent space).  Output: normalised partial O [B,H,512] and LSE [B,H].
 //
 // Design for gfx950:
-//  * A work-group owns 64 query heads (NPAIR = 2) or 32 (NPAIR = 1) and a
-//    token-balanced span of the rank's tiles (32 tokens each).  Every latent row is
-//    read from HBM once per head group and used as both K and V.
-//  * Tiles stream HBM -> LDS with 16-byte direct-to-LDS loads through an NSTAGE ring;
-//    no VGPRs are spent on staging, so the loads of the next stages stay in flight
-//    while the current tile is computed.  Row chunks are rotated by the row index in
-//    LDS so the MFMA operand reads of 32 rows hit distinct banks.
-//  * Waves come in pairs that share 32 heads.  QK^T (contraction 576) is split by
-//    dimension halves across the pair (each wave keeps its 32 x 288 slice of q in
-//    VGPRs); the two 32x32 fp32 score halves are summed through LDS.  PV is split by
-//    output halves (each wave accumulates O^T for 256 of the 512 dims).
-//  * Both contractions use v_mfma_f32_32x32x16_bf16.  S^T = K Q^T puts tokens on the
-//    MFMA rows and heads on the columns, so each lane's softmax statistics belong to
-//    one head; the S^T accumulator, converted to bf16, is directly the B operand of
-//    O^T += V^T P^T.  V^T comes from LDS through the transposing ds_read_b64_tr_b16.
-//  * Online softmax in base 2 with fp32 statistics; the O accumulator is rescaled
-//    only when some head's running maximum moved.
+//  * A work-group owns up to 64 query heads (4 waves x 16 heads) and a
+//    token-balanced span of the rank's 32-token tiles; the span may cover the end
+//    of one request, whole requests and the start of another.  Every latent row is
+//    read from HBM once per head group and serves as both K and V.
+//  * Tiles stream HBM -> LDS through a 4-stage ring of 16-byte direct-to-LDS copies
+//    (no VGPR staging), issued three tiles ahead and continuing across request
+//    boundaries.  LDS rows are padded to an odd stride of 73 16-byte slots, which
+//    keeps the 16-row MFMA operand reads free of bank conflicts with affine
+//    addresses; operand reads are software-pipelined a few MFMA steps ahead.
+//  * Each wave owns 16 heads over the full 576 dims, so waves never exchange
+//    partial scores: S^T = K Q^T (two 16x16x32 bf16 MFMA chains, tokens on the
+//    rows, heads on the columns; the wave's 16 x 576 q slice lives in VGPRs), then
+//    base-2 online softmax whose statistics are lane-local per head, then
+//    O^T += V^T P^T where the S^T accumulator converted to bf16 is the B operand
+//    and V^T comes from LDS through the transposing ds_read_b64_tr_b16.
+//  * The running maximum moves only when a tile's maximum exceeds it by more than
+//    kRescaleSlack (log2 units), so the 128-register O accumulator is rarely
+//    rescaled; P stays <= 2^kRescaleSlack and the final LSE uses the same maximum,
+//    so the result is unchanged.
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -32,236 +34,318 @@ namespace mla {
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
-constexpr int kRowBytes = kDqk * 2;        // 1152
-constexpr int kChunks = kRowBytes / 16;    // 72 16-byte chunks per row
-constexpr int kTile = 32;                  // tokens per tile
-constexpr int kTileBytes = kTile * kRowBytes;  // 36864
-constexpr int kStages = 3;
-constexpr int kXchgBytes = 64 * 16 * 4;    // one wave's 32x32 fp32 score half
-constexpr int kQSteps = kDqk / 2 / 16;     // 18 k-steps of 16 dims per half
+constexpr int kRowBytes = kDqk * 2;            // 1152
+constexpr int kChunks = kRowBytes / 16;        // 72 16-byte chunks per row
+constexpr int kTile = 32;                      // tokens per tile
+constexpr int kRowSlots = kChunks + 1;         // 73: odd LDS row stride in 16-byte slots
+constexpr int kLdsRowBytes = kRowSlots * 16;   // 1168
+constexpr int kTileSlots = kTile * kRowSlots;  // 2336
+constexpr int kTileBytes = kTileSlots * 16;    // 37376
+constexpr int kStages = 4;
+constexpr int kPrefetch = 4;                   // LDS operand reads issued this many steps ahead
+constexpr int kKSteps = kDqk / 32;             // 18 k-steps of 32 dims
+constexpr int kVTiles = kDv / 16;              // 32 O^T tiles of 16 dims
+constexpr float kRescaleSlack = 8.0f;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
-// LDS byte offset of 16-byte chunk c of tile row `row` (rotated placement).
-__device__ __forceinline__ int chunk_off(int row, int c) {
-  int pc = c + row;
-  pc = pc >= kChunks ? pc - kChunks : pc;
-  return row * kRowBytes + pc * 16;
-}
+// LDS byte offset of 16-byte chunk c of tile row `row`.  Rows are kRowSlots = 73
+// slots apart: an odd stride puts the same chunk of 16 consecutive rows in 16
+// different 4-bank groups (no conflicts), while every operand address stays
+// affine in the chunk index (one base register plus an immediate offset).
+__device__ __forceinline__ constexpr int chunk_off(int row, int c) { return row * kLdsRowBytes + c * 16; }
 
-template <int NPAIR>
+template <int NW>
 struct Cfg {
-  static constexpr int kWaves = 2 * NPAIR;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kHeads = 32 * NPAIR;
-  static constexpr int kLoads = kTile * kChunks / kThreads;  // DMA loads per thread per tile
-  static_assert(kTile * kChunks % kThreads == 0, "tile must split evenly");
-  static constexpr int kLdsBytes = kStages * kTileBytes + kWaves * kXchgBytes;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kHeads = 16 * NW;
+  // A tile is kTileSlots 16-byte slots written 64 at a time (one DMA instruction of a
+  // wave); instruction j = k * NW + wave covers slots [64 j, 64 j + 64).  The slot
+  // count is not a multiple of 64 * NW, so wave 0 issues one more (partly masked)
+  // instruction than the others.
+  static constexpr int kInstr = (kTileSlots + 63) / 64;        // 37
+  static constexpr int kLoadsMax = (kInstr + NW - 1) / NW;     // per wave, wave 0
+  static constexpr int kLoadsMin = kInstr / NW;                // the other waves
+  static_assert(kLoadsMax * (kStages - 2) < 64, "vmcnt range");
 };
 
-template <int NPAIR>
-__global__ __launch_bounds__(128 * NPAIR, 1) void mla_partial_kernel(PartialParams p) {
-  using C = Cfg<NPAIR>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
+// Position in the span's sequence of (request, tile) pairs.
+struct Cursor {
+  int b;
+  int64_t t, ntile, Lr;
+};
+
+__device__ __forceinline__ void cursor_set(Cursor& c, const PartitionArgs& a, int b, int64_t t) {
+  c.b = b;
+  c.t = t;
+  c.Lr = part_local_len(a, b);
+  c.ntile = (c.Lr + kTile - 1) / kTile;
+}
+
+// Advance to the next tile; only called while the span has tiles left, so a
+// non-empty request follows whenever the current one is exhausted.
+__device__ __forceinline__ void cursor_next(Cursor& c, const PartitionArgs& a) {
+  if (++c.t < c.ntile) return;
+  do {
+    ++c.b;
+    c.Lr = part_local_len(a, c.b);
+    c.ntile = (c.Lr + kTile - 1) / kTile;
+  } while (c.ntile == 0 && c.b + 1 < a.batch);
+  c.t = 0;
+}
+
+// Wait until the DMA copies of the current tile have landed: `after` tiles were
+// issued after it (NL copy instructions each from this wave), and any younger
+// memory operation only makes the wait stricter.
+template <int NL>
+__device__ __forceinline__ void wait_tile(int64_t after) {
+  if (after >= 2) wait_vmcnt_builtin<2 * NL>();
+  else if (after == 1) wait_vmcnt_builtin<NL>();
+  else wait_vmcnt_builtin<0>();
+}
+
+template <int NW>
+__device__ __forceinline__ void wait_tile_wave(int wave, int64_t after) {
+  if (Cfg<NW>::kLoadsMax != Cfg<NW>::kLoadsMin && wave < Cfg<NW>::kInstr % NW)
+    wait_tile<Cfg<NW>::kLoadsMax>(after);
+  else
+    wait_tile<Cfg<NW>::kLoadsMin>(after);
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p) {
+  using C = Cfg<NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
   __shared__ int64_t s_scan[C::kThreads];
   __shared__ int64_t s_loc[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int pair = wave >> 1;
-  const int half = wave & 1;     // QK dims [288*half, +288); O dims [256*half, +256)
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;      // 0/1: which half of the wave
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
 
   int64_t w;
   int hg;
   block_to_span(p.part.num_parts, p.num_head_groups, &w, &hg);
   const bool write_prefix = (w == 0 && hg == 0);
-  SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr, s_scan,
-                                         s_loc);
+  const SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
+                                               s_scan, s_loc);
   if (loc.start >= loc.end) return;
+  const int64_t total = loc.end - loc.start;
 
   const int H = p.num_q_heads;
-  const int head = hg * C::kHeads + pair * 32 + l32;   // this lane's head (S^T column)
+  const int head = hg * C::kHeads + wave * 16 + l16;  // this lane's head (S^T column)
   const bool head_ok = head < H;
-
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
-  DCP_LDS uint8_t* xbuf = lds + kStages * kTileBytes;
 
-  // Per-lane source offsets of the DMA loads inside a tile (row-major 1152-byte rows).
-  int ld_row[C::kLoads];
-  int ld_off[C::kLoads];
+  // This lane's DMA copies: LDS slot (k * NW + wave) * 64 + lane of every tile
+  // holds chunk (slot % 73) of row (slot / 73); the 73rd slot of a row and slots
+  // past the tile are left unwritten.
+  int ld_row[C::kLoadsMax];
+  int ld_off[C::kLoadsMax];
+  bool ld_ok[C::kLoadsMax];
 #pragma unroll
-  for (int k = 0; k < C::kLoads; ++k) {
-    const int s = (k * C::kWaves + wave) * 64 + lane;   // LDS slot of this lane's chunk
-    const int row = s / kChunks;
-    const int pc = s - row * kChunks;
-    int c = pc - row;
-    c = c < 0 ? c + kChunks : c;
+  for (int k = 0; k < C::kLoadsMax; ++k) {
+    const int s = (k * NW + wave) * 64 + lane;
+    const int row = s / kRowSlots;
+    const int c = s - row * kRowSlots;
+    ld_ok[k] = s < kTileSlots && c < kChunks;
     ld_row[k] = row;
     ld_off[k] = row * kRowBytes + c * 16;
   }
 
-  int64_t remaining = loc.end - loc.start;
-  int b = loc.b0;
-  int64_t toff = loc.off0;
+  Cursor lc, cc;
+  cursor_set(lc, p.part, loc.b0, loc.off0);
+  cc = lc;
+
+  auto issue = [&](int stage) {
+    const int64_t tok0 = lc.t * kTile;
+    const int32_t* bt_row = p.block_table + (int64_t)lc.b * p.max_blocks_per_seq;
+    const int32_t page = clamp_page(ld_const(bt_row + tok0 / p.block_size), p.num_cache_blocks);
+    const int64_t slot0 = tok0 % p.block_size;
+    const int nvalid = (int)((lc.Lr - tok0) < kTile ? (lc.Lr - tok0) : kTile);
+    const uint8_t* base = p.k_cache + ((int64_t)page * p.block_size + slot0) * kRowBytes;
+    DCP_LDS uint8_t* dst = lds + stage * kTileBytes;
+#pragma unroll
+    for (int k = 0; k < C::kLoadsMax; ++k) {
+      if (k * NW + wave >= C::kInstr) continue;   // wave-uniform: this wave has one copy fewer
+      int off = ld_off[k];
+      if (ld_row[k] >= nvalid) off -= (ld_row[k] - (nvalid - 1)) * kRowBytes;  // repeat last row
+      if (ld_ok[k]) dma16(base + off, dst + (k * NW + wave) * 1024);
+    }
+  };
+
+  // q[b, head, 32*s + 8*q4 .. +7]: the B operand of S^T = K Q^T for k-step s.
+  bf16x8 qreg[kKSteps];
+  auto load_q = [&](int b) {
+    const uint16_t* qp = p.q + ((int64_t)b * H + (head_ok ? head : 0)) * kDqk + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+      bf16x8 v = *(const bf16x8*)(qp + 32 * s);
+      qreg[s] = head_ok ? v : bf16x8{};
+    }
+    // The q slice is only an MFMA operand: keep it in accumulation registers so the
+    // VGPRs stay free for the O accumulator and the operand prefetch ring.
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+a"(qreg[s]));
+  };
+
+  // prologue: up to kStages-1 tiles in flight
+  int64_t issued = 0;
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (issued < total) {
+      issue(s);
+      if (++issued < total) cursor_next(lc, p.part);
+    }
+  }
+  load_q(cc.b);
+
+  f32x4 oacc[kVTiles];
+#pragma unroll
+  for (int m = 0; m < kVTiles; ++m) oacc[m] = f32x4{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  int64_t piece_t0 = cc.t;  // first tile of the current piece inside request cc.b
   bool first_piece = true;
 
-  while (remaining > 0) {
-    const int64_t Lr = part_local_len(p.part, b);
-    const int64_t ntile = (Lr + kTile - 1) / kTile;
-    if (ntile == 0) { ++b; continue; }
-    const int64_t n = (ntile - toff) < remaining ? (ntile - toff) : remaining;
-    const bool whole = (toff == 0 && n == ntile);
-    const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+  for (int64_t i = 0; i < total; ++i) {
+    wait_tile_wave<NW>(wave, issued - 1 - i);
+    wg_barrier();
+    if (issued < total) {
+      issue((int)(issued % kStages));
+      if (++issued < total) cursor_next(lc, p.part);
+    }
 
-    // ---- query slice of this wave: q[b, head, 288*half + 16*s + 8*hi .. +7]
-    bf16x8 qreg[kQSteps];
+    const DCP_LDS uint8_t* tb = lds + (int)(i % kStages) * kTileBytes;
+    const int64_t tok0 = cc.t * kTile;
+    const int nvalid = (int)((cc.Lr - tok0) < kTile ? (cc.Lr - tok0) : kTile);
+
+    // ---- S^T [32 tokens x 16 heads] = K [32 x 576] Q^T, as two 16-token chains.
+    // Operand reads run kPrefetch k-steps ahead of the MFMAs.
+    f32x4 s0 = f32x4{}, s1 = f32x4{};
     {
-      const uint16_t* qp = p.q + ((int64_t)b * H + (head_ok ? head : 0)) * kDqk + 288 * half + 8 * hi;
+      const DCP_LDS uint8_t* ka = tb + chunk_off(l16, q4);   // + 64 * s (+ 16 rows)
+      bf16x8 r0[kPrefetch], r1[kPrefetch];
 #pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        bf16x8 v = *(const bf16x8*)(qp + 16 * s);
-        if (!head_ok) v = bf16x8{};
-        qreg[s] = v;
+      for (int s = 0; s < kPrefetch; ++s) {
+        r0[s] = *(const DCP_LDS bf16x8*)(ka + 64 * s);
+        r1[s] = *(const DCP_LDS bf16x8*)(ka + 16 * kLdsRowBytes + 64 * s);
       }
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const bf16x8 a0 = r0[s % kPrefetch];
+        const bf16x8 a1 = r1[s % kPrefetch];
+        if (s + kPrefetch < kKSteps) {
+          r0[s % kPrefetch] = *(const DCP_LDS bf16x8*)(ka + 64 * (s + kPrefetch));
+          r1[s % kPrefetch] = *(const DCP_LDS bf16x8*)(ka + 16 * kLdsRowBytes + 64 * (s + kPrefetch));
+        }
+        s0 = mfma16x16x32(a0, qreg[s], s0);
+        s1 = mfma16x16x32(a1, qreg[s], s1);
+      }
+      // Keep 2*kPrefetch operand reads in flight: reads first, then (2 MFMA, 2 reads) ...
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetch, 0);
+#pragma unroll
+      for (int s = 0; s < kKSteps - kPrefetch; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPrefetch, 0);
     }
 
-    auto issue_tile = [&](int64_t t_local, int stage) {
-      const int64_t tok0 = t_local * kTile;
-      const int32_t page = clamp_page(ld_const(bt_row + tok0 / p.block_size), p.num_cache_blocks);
-      const int64_t slot0 = tok0 % p.block_size;
-      const int nvalid = (int)((Lr - tok0) < kTile ? (Lr - tok0) : kTile);
-      const uint8_t* base = p.k_cache + ((int64_t)page * p.block_size + slot0) * kRowBytes;
-      DCP_LDS uint8_t* dst = lds + stage * kTileBytes;
+    // ---- online softmax (base 2).  Lane: head l16, tokens 16*(j/4) + 4*q4 + j%4.
+    float x[8];
+    float mloc = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < C::kLoads; ++k) {
-        int off = ld_off[k];
-        if (ld_row[k] >= nvalid) off -= (ld_row[k] - (nvalid - 1)) * kRowBytes;  // replicate last row
-        dma16(base + off, dst + (k * C::kWaves + wave) * 1024);
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * q4 + (j & 3);
+      const float sv = j < 4 ? s0[j] : s1[j - 4];
+      x[j] = tok < nvalid ? sv * p.scale_log2 : -INFINITY;
+      mloc = fmaxf(mloc, x[j]);
+    }
+    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+    const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    float lsum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pr = fast_exp2(x[j] - m_new);
+      lsum += pr;
+      pb[j] = (__bf16)pr;
+    }
+    lsum += shfl_xor_f(lsum, 16);
+    lsum += shfl_xor_f(lsum, 32);
+    l_run = l_run * alpha + lsum;
+    if (__any(m_new != m_run)) {
+#pragma unroll
+      for (int m = 0; m < kVTiles; ++m) oacc[m] *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] P^T [32 x 16].
+    // Source lane l16 of each 16-lane group addresses row 4*q4 + l16/4 (and +16),
+    // dims 16m + 4*(l16%4) .. +3, i.e. chunk 2m + (l16%4)/2, half (l16%2).
+    {
+      const DCP_LDS uint8_t* va = tb + chunk_off(4 * q4 + (l16 >> 2), (l16 & 3) >> 1) + (l16 & 1) * 8;
+      u32x2 v1[kPrefetch], v2[kPrefetch];
+#pragma unroll
+      for (int m = 0; m < kPrefetch; ++m) {
+        v1[m] = lds_read_tr16(va + 32 * m);
+        v2[m] = lds_read_tr16(va + 16 * kLdsRowBytes + 32 * m);
       }
-    };
-
-    f32x16 oacc[8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) oacc[m] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    // prologue
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < n) issue_tile(toff + s, s);
-
-    for (int64_t i = 0; i < n; ++i) {
-      if (i + kStages - 2 < n) wait_vmcnt<C::kLoads * (kStages - 2)>();
-      else wait_vmcnt<0>();
-      wg_barrier();
-      if (i + kStages - 1 < n) issue_tile(toff + i + kStages - 1, (int)((i + kStages - 1) % kStages));
-
-      const DCP_LDS uint8_t* tb = lds + (int)(i % kStages) * kTileBytes;
-      const int64_t tok0 = (toff + i) * kTile;
-      const int nvalid = (int)((Lr - tok0) < kTile ? (Lr - tok0) : kTile);
-
-      // ---- S^T half = K[:, half dims] . Q^T   (rows = tokens, cols = heads)
-      f32x16 sacc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < kQSteps; ++s) {
-        const int c = 36 * half + 2 * s + hi;
-        const bf16x8 a = *(const DCP_LDS bf16x8*)(tb + chunk_off(l32, c));
-        sacc = mfma32x32x16(a, qreg[s], sacc);
+      for (int m = 0; m < kVTiles; ++m) {
+        const bf16x8 a = join_tr16(v1[m % kPrefetch], v2[m % kPrefetch]);
+        if (m + kPrefetch < kVTiles) {
+          v1[m % kPrefetch] = lds_read_tr16(va + 32 * (m + kPrefetch));
+          v2[m % kPrefetch] = lds_read_tr16(va + 16 * kLdsRowBytes + 32 * (m + kPrefetch));
+        }
+        oacc[m] = mfma16x16x32(a, pb, oacc[m]);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetch, 1);
+#pragma unroll
+      for (int m = 0; m < kVTiles - kPrefetch; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 1);
+    }
 
-      // ---- sum the two dimension halves of the pair through LDS
-      DCP_LDS f32x4* xw = (DCP_LDS f32x4*)(xbuf + wave * kXchgBytes);
-      DCP_LDS f32x4* xp = (DCP_LDS f32x4*)(xbuf + (wave ^ 1) * kXchgBytes);
+    // ---- end of a request piece: normalise and store, then move to the next request
+    const bool last_of_req = cc.t == cc.ntile - 1;
+    if (last_of_req || i == total - 1) {
+      const bool whole = piece_t0 == 0 && last_of_req;
+      if (head_ok) {
+        const float inv = 1.0f / l_run;
+        const int64_t slot = 2 * w + (first_piece ? 0 : 1);
+        float* orow = whole ? p.out_o + ((int64_t)cc.b * H + head) * kDv
+                            : p.ws_o + (slot * H + head) * kDv;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xw[j * 64 + lane] = f32x4{sacc[4 * j], sacc[4 * j + 1], sacc[4 * j + 2], sacc[4 * j + 3]};
-      wg_barrier();
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 o = xp[j * 64 + lane];
-        sacc[4 * j] += o[0];
-        sacc[4 * j + 1] += o[1];
-        sacc[4 * j + 2] += o[2];
-        sacc[4 * j + 3] += o[3];
-      }
-
-      // ---- online softmax (base 2).  Lane holds head `head`, tokens 8(r/4)+4*hi+(r%4).
-      float x[16];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = 8 * (r >> 2) + 4 * hi + (r & 3);
-        x[r] = tok < nvalid ? sacc[r] * p.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, x[r]);
-      }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = fast_exp2(m_run - m_new);
-      float lsum = 0.f;
-      bf16x8 pb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(x[r] - m_new);
-        lsum += pr;
-        pb[r >> 3][r & 7] = (__bf16)pr;
-      }
-      lsum += shfl_xor_f(lsum, 32);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
-      }
-
-      // ---- O^T[256*half .. +256, heads] += V^T P^T over the 32 tokens
-      const int grp = (lane >> 4) & 1;
-      const int sl = lane & 15;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int d0 = 256 * half + 32 * m + 16 * grp + 4 * (sl & 3);   // source lane's 4 dims
-          const int c = d0 >> 3;
-          const int hb = (d0 & 4) * 2;                                    // byte offset in chunk
-          const int r1 = 16 * ks + 4 * hi + (sl >> 2);
-          const int r2 = r1 + 8;
-          const u32x2 v1 = lds_read_tr16(tb + chunk_off(r1, c) + hb);
-          const u32x2 v2 = lds_read_tr16(tb + chunk_off(r2, c) + hb);
-          const bf16x8 a = join_tr16(v1, v2);
-          oacc[m] = mfma32x32x16(a, pb[ks], oacc[m]);
+        for (int m = 0; m < kVTiles; ++m) *(f32x4*)(orow + 16 * m + 4 * q4) = oacc[m] * inv;
+        if (q4 == 0) {
+          const float lse = (m_run + fast_log2(l_run)) * kLn2;
+          if (whole) p.out_lse[(int64_t)cc.b * H + head] = lse;
+          else p.ws_lse[slot * H + head] = lse;
         }
       }
-    }
-    wg_barrier();  // every wave is done with the ring and the exchange buffers
-
-    // ---- epilogue: normalise and store.  oacc[m] lane reg r -> dim 256*half + 32m + 8(r/4) + 4*hi + r%4
-    if (head_ok) {
-      const float inv = 1.0f / l_run;
-      const float lse = (m_run + fast_log2(l_run)) * kLn2;
-      const int64_t slot = 2 * w + (first_piece ? 0 : 1);
-      float* orow = whole ? p.out_o + ((int64_t)b * H + head) * kDv
-                          : p.ws_o + (slot * H + head) * kDv;
+      if (i + 1 < total) {
+        cursor_next(cc, p.part);
+        piece_t0 = 0;
+        first_piece = false;
+        load_q(cc.b);
+        wait_vmcnt_builtin<0>();
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 256 * half + 32 * m + 8 * j + 4 * hi;
-          *(f32x4*)(orow + d) = f32x4{oacc[m][4 * j] * inv, oacc[m][4 * j + 1] * inv,
-                                      oacc[m][4 * j + 2] * inv, oacc[m][4 * j + 3] * inv};
-        }
+        for (int m = 0; m < kVTiles; ++m) oacc[m] = f32x4{};
+        m_run = -INFINITY;
+        l_run = 0.f;
       }
-      if (half == 0 && hi == 0) {
-        if (whole) p.out_lse[(int64_t)b * H + head] = lse;
-        else p.ws_lse[slot * H + head] = lse;
-      }
+    } else {
+      cursor_next(cc, p.part);
     }
-
-    remaining -= n;
-    first_piece = false;
-    ++b;
-    toff = 0;
   }
 }
 
@@ -272,9 +356,9 @@ int mla_heads_per_group(int num_q_heads) { return num_q_heads <= 32 ? 32 : 64; }
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;
   if (mla_heads_per_group(p.num_q_heads) == 32)
-    hipLaunchKernelGGL(mla::mla_partial_kernel<1>, dim3(grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(mla::mla_partial_kernel<2>, dim3(grid), dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(mla::mla_partial_kernel<2>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla::mla_partial_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -14,24 +14,35 @@ namespace dcp {
 
 // ------------------------------------------------------------------ split-K reduce
 // One block of 256 threads per (request, group of heads); each thread owns 4
-// consecutive floats of one head's v_dim outputs (DV/4 threads per head).
+// consecutive floats of one head's v_dim outputs (DV/4 threads per head).  The
+// pieces' slots and LSEs are first staged in LDS by the whole block, then every
+// thread folds the pieces in with eight independent loads in flight; pieces are
+// taken 256 at a time with an online maximum, so any count works.
 template <int DV>
 __global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceParams p) {
   constexpr int kTph = DV / 4;         // threads per head
   constexpr int kHpb = 256 / kTph;     // heads per block
+  constexpr int kChunk = 256;          // pieces staged per round
+  constexpr int kUnroll = 8;
   static_assert(256 % kTph == 0, "head rows must tile the block");
+  __shared__ int64_t s_slot[kChunk];
+  __shared__ float s_lse[kChunk][kHpb];
+
   const int b = blockIdx.x;
-  const int head = blockIdx.y * kHpb + (int)threadIdx.x / kTph;
+  const int head0 = blockIdx.y * kHpb;
+  const int hd = (int)threadIdx.x / kTph;
+  const int head = head0 + hd;
   const int t = threadIdx.x % kTph;
   const int H = p.num_heads;
-  if (head >= H) return;
 
   const int64_t F = p.ws_prefix[b];
   const int64_t n = p.ws_prefix[b + 1] - F;
   float* orow = p.out_o + ((int64_t)b * H + head) * DV + 4 * t;
   if (n == 0) {
-    *(f32x4*)orow = f32x4{};
-    if (t == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
+    if (head < H) {
+      *(f32x4*)orow = f32x4{};
+      if (t == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
+    }
     return;
   }
   const int64_t TT = p.ws_prefix[p.batch];
@@ -40,23 +51,48 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceParams p) 
   const int64_t w_hi = span_of(F + n - 1, TT, P);
   if (w_lo == w_hi) return;  // computed in one piece by the partial kernel
 
-  float mx = -INFINITY;
-  for (int64_t w = w_lo; w <= w_hi; ++w) {
-    const int64_t s0 = span_start(w, TT, P);
-    if (s0 == span_start(w + 1, TT, P)) continue;  // empty span
-    const int64_t slot = 2 * w + (s0 < F ? 1 : 0);
-    mx = fmaxf(mx, p.ws_lse[slot * H + head]);
-  }
+  float mx = -INFINITY, wsum = 0.f;
   f32x4 acc = f32x4{};
-  float wsum = 0.f;
-  for (int64_t w = w_lo; w <= w_hi; ++w) {
-    const int64_t s0 = span_start(w, TT, P);
-    if (s0 == span_start(w + 1, TT, P)) continue;
-    const int64_t slot = 2 * w + (s0 < F ? 1 : 0);
-    const float wt = fast_exp2((p.ws_lse[slot * H + head] - mx) * kLog2e);
-    wsum += wt;
-    acc += wt * *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * t);
+  for (int64_t base = w_lo; base <= w_hi; base += kChunk) {
+    const int cnt = (int)((w_hi - base + 1) < kChunk ? (w_hi - base + 1) : kChunk);
+    __syncthreads();  // previous round's LDS reads are done
+    for (int i = threadIdx.x; i < cnt; i += 256) {
+      const int64_t w = base + i;
+      const int64_t s0 = span_start(w, TT, P);
+      const bool empty = s0 == span_start(w + 1, TT, P);
+      const int64_t slot = empty ? -1 : 2 * w + (s0 < F ? 1 : 0);
+      s_slot[i] = slot;
+#pragma unroll
+      for (int h = 0; h < kHpb; ++h)
+        s_lse[i][h] = (slot >= 0 && head0 + h < H) ? p.ws_lse[slot * H + head0 + h] : -INFINITY;
+    }
+    __syncthreads();
+    if (head >= H) continue;
+    float cm = -INFINITY;
+    for (int i = 0; i < cnt; ++i) cm = fmaxf(cm, s_lse[i][hd]);
+    const float nm = fmaxf(mx, cm);
+    const float rescale = mx == -INFINITY ? 0.f : fast_exp2((mx - nm) * kLog2e);
+    acc *= rescale;
+    wsum *= rescale;
+    mx = nm;
+    for (int i0 = 0; i0 < cnt; i0 += kUnroll) {
+      f32x4 v[kUnroll];
+      float wt[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int i = i0 + u;
+        const int64_t slot = i < cnt ? s_slot[i] : -1;
+        wt[u] = slot >= 0 ? fast_exp2((s_lse[i][hd] - mx) * kLog2e) : 0.f;
+        v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * t) : f32x4{};
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        wsum += wt[u];
+        acc += wt[u] * v[u];
+      }
+    }
   }
+  if (head >= H) return;
   *(f32x4*)orow = acc * (1.0f / wsum);
   if (t == 0) p.out_lse[(int64_t)b * H + head] = mx + fast_log2(wsum) * kLn2;
 }
