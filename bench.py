@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle math to time for the CPU baseline")
+    ap.add_argument("--copy-probe-bytes", type=int, default=0,
+                    help="before timing, run one plain device-to-device copy of this many bytes "
+                         "(a reference for scaling the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -151,6 +154,13 @@ def main():
         dcp.dcp_merge(o_all, l_all, o, lse)
         if evs is not None:
             evs[N][1].record()
+
+    if args.copy_probe_bytes:
+        src = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

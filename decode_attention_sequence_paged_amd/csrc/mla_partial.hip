@@ -56,6 +56,13 @@ constexpr int kSchedDsRead = 0x100;
 // affine in the chunk index (one base register plus an immediate offset).
 __device__ __forceinline__ constexpr int chunk_off(int row, int c) { return row * kLdsRowBytes + c * 16; }
 
+// Token (= LDS row) behind row i of a 16-row MFMA tile: rows 0..7 take the even
+// tokens, rows 8..15 the odd ones.  The transposing read of V serves 32 lanes per
+// LDS pass, i.e. lane groups q4 = {0,1} and {2,3}; with this order each pass reads 8
+// rows of one parity, whose 32-byte pieces fall into disjoint banks at the 73-slot
+// stride, and the 16 rows of an S^T tile stay distinct modulo 16 for the QK reads.
+__device__ __forceinline__ constexpr int tile_row(int i) { return i < 8 ? 2 * i : 2 * (i - 8) + 1; }
+
 template <int NW>
 struct Cfg {
   static constexpr int kThreads = 64 * NW;
@@ -65,52 +72,60 @@ struct Cfg {
   // count is not a multiple of 64 * NW, so wave 0 issues one more (partly masked)
   // instruction than the others.
   static constexpr int kInstr = (kTileSlots + 63) / 64;        // 37
-  static constexpr int kLoadsMax = (kInstr + NW - 1) / NW;     // per wave, wave 0
-  static constexpr int kLoadsMin = kInstr / NW;                // the other waves
+  static constexpr int kMainCopies = (kInstr - 1) / NW;        // full instructions per wave
+  static constexpr int kTailLanes = kTileSlots - (kInstr - 1) * 64;  // 32 lanes of the last one
+  static_assert((kInstr - 1) % NW == 0, "full copy instructions must split evenly over waves");
+  static constexpr int kLoadsMax = kMainCopies + 1;            // wave 0
+  static constexpr int kLoadsMin = kMainCopies;                // the other waves
   static_assert(kLoadsMax * (kStages - 2) < 64, "vmcnt range");
 };
 
-// Position in the span's sequence of (request, tile) pairs.
+// Position in the span's sequence of (request, tile) pairs, 32-bit and division
+// free inside the loop: the page of tile t is entry pk of the request's block-table
+// row and the tile starts at token 32 * sub of that page (tpp tiles per page).
 struct Cursor {
-  int b;
-  int64_t t, ntile, Lr;
+  int b, t, ntile, Lr, pk, sub;
+  const int32_t* bt_row;
 };
 
-__device__ __forceinline__ void cursor_set(Cursor& c, const PartitionArgs& a, int b, int64_t t) {
+__device__ __forceinline__ void cursor_request(Cursor& c, const PartialParams& p, int b) {
   c.b = b;
-  c.t = t;
-  c.Lr = part_local_len(a, b);
+  c.Lr = (int)part_local_len(p.part, b);
   c.ntile = (c.Lr + kTile - 1) / kTile;
+  c.bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+}
+
+__device__ __forceinline__ void cursor_set(Cursor& c, const PartialParams& p, int tpp, int b, int t) {
+  cursor_request(c, p, b);
+  c.t = t;
+  c.pk = t / tpp;
+  c.sub = t - c.pk * tpp;
 }
 
 // Advance to the next tile; only called while the span has tiles left, so a
 // non-empty request follows whenever the current one is exhausted.
-__device__ __forceinline__ void cursor_next(Cursor& c, const PartitionArgs& a) {
-  if (++c.t < c.ntile) return;
-  do {
-    ++c.b;
-    c.Lr = part_local_len(a, c.b);
-    c.ntile = (c.Lr + kTile - 1) / kTile;
-  } while (c.ntile == 0 && c.b + 1 < a.batch);
-  c.t = 0;
+__device__ __forceinline__ void cursor_next(Cursor& c, const PartialParams& p, int tpp) {
+  ++c.t;
+  if (++c.sub == tpp) { c.sub = 0; ++c.pk; }
+  if (c.t < c.ntile) return;
+  do cursor_request(c, p, c.b + 1); while (c.ntile == 0 && c.b + 1 < p.part.batch);
+  c.t = c.pk = c.sub = 0;
 }
 
-// Wait until the DMA copies of the current tile have landed: `after` tiles were
-// issued after it (NL copy instructions each from this wave), and any younger
-// memory operation only makes the wait stricter.
-template <int NL>
-__device__ __forceinline__ void wait_tile(int64_t after) {
-  if (after >= 2) wait_vmcnt_builtin<2 * NL>();
-  else if (after == 1) wait_vmcnt_builtin<NL>();
-  else wait_vmcnt_builtin<0>();
+// Cross-lane reductions over the lanes l, l^16, l^32, l^48 (one head's four lane
+// groups) with the gfx950 row-swap permutes: applying the operation to the two
+// outputs of a swap of x with itself combines x with its partner lane.
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
 }
-
-template <int NW>
-__device__ __forceinline__ void wait_tile_wave(int wave, int64_t after) {
-  if (Cfg<NW>::kLoadsMax != Cfg<NW>::kLoadsMin && wave < Cfg<NW>::kInstr % NW)
-    wait_tile<Cfg<NW>::kLoadsMax>(after);
-  else
-    wait_tile<Cfg<NW>::kLoadsMin>(after);
+__device__ __forceinline__ float sum_over_groups(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
 template <int NW>
@@ -133,7 +148,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   const SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
                                                s_scan, s_loc);
   if (loc.start >= loc.end) return;
-  const int64_t total = loc.end - loc.start;
+  const int total = (int)(loc.end - loc.start);
+  const int tpp = p.block_size / kTile;                    // tiles per page
+  const int64_t page_bytes = (int64_t)p.block_size * kRowBytes;
+  // DMA copy instructions this wave issues per tile (wave 0 has the extra one).
+  const bool extra_copy = wave == 0;
 
   const int H = p.num_q_heads;
   const int head = hg * C::kHeads + wave * 16 + l16;  // this lane's head (S^T column)
@@ -141,39 +160,50 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
   // This lane's DMA copies: LDS slot (k * NW + wave) * 64 + lane of every tile
-  // holds chunk (slot % 73) of row (slot / 73); the 73rd slot of a row and slots
-  // past the tile are left unwritten.
-  int ld_row[C::kLoadsMax];
-  int ld_off[C::kLoadsMax];
-  bool ld_ok[C::kLoadsMax];
+  // holds chunk (slot % 73) of row (slot / 73).  The 73rd slot of a row is never
+  // read; its lane copies the row's last chunk again (same cache line) instead of
+  // branching.  Every wave issues kMainCopies full instructions; wave 0 adds the
+  // half-filled tail instruction, whose lanes past the tile are masked.
+  int ld_row[C::kMainCopies];
+  int ld_off[C::kMainCopies];
 #pragma unroll
-  for (int k = 0; k < C::kLoadsMax; ++k) {
+  for (int k = 0; k < C::kMainCopies; ++k) {
     const int s = (k * NW + wave) * 64 + lane;
     const int row = s / kRowSlots;
     const int c = s - row * kRowSlots;
-    ld_ok[k] = s < kTileSlots && c < kChunks;
     ld_row[k] = row;
-    ld_off[k] = row * kRowBytes + c * 16;
+    ld_off[k] = row * kRowBytes + (c < kChunks ? c : kChunks - 1) * 16;
   }
+  int tail_row, tail_off;
+  {
+    const int s = C::kMainCopies * NW * 64 + lane;
+    tail_row = s / kRowSlots;
+    const int c = s - tail_row * kRowSlots;
+    tail_off = tail_row * kRowBytes + (c < kChunks ? c : kChunks - 1) * 16;
+  }
+  const bool tail_lane = wave == 0 && lane < C::kTailLanes;
 
   Cursor lc, cc;
-  cursor_set(lc, p.part, loc.b0, loc.off0);
+  cursor_set(lc, p, tpp, loc.b0, (int)loc.off0);
   cc = lc;
 
   auto issue = [&](int stage) {
-    const int64_t tok0 = lc.t * kTile;
-    const int32_t* bt_row = p.block_table + (int64_t)lc.b * p.max_blocks_per_seq;
-    const int32_t page = clamp_page(ld_const(bt_row + tok0 / p.block_size), p.num_cache_blocks);
-    const int64_t slot0 = tok0 % p.block_size;
-    const int nvalid = (int)((lc.Lr - tok0) < kTile ? (lc.Lr - tok0) : kTile);
-    const uint8_t* base = p.k_cache + ((int64_t)page * p.block_size + slot0) * kRowBytes;
+    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    const uint8_t* base = p.k_cache + page * page_bytes + lc.sub * (kTile * kRowBytes);
     DCP_LDS uint8_t* dst = lds + stage * kTileBytes;
+    const int nvalid = lc.Lr - lc.t * kTile;
+    if (nvalid >= kTile) {
 #pragma unroll
-    for (int k = 0; k < C::kLoadsMax; ++k) {
-      if (k * NW + wave >= C::kInstr) continue;   // wave-uniform: this wave has one copy fewer
-      int off = ld_off[k];
-      if (ld_row[k] >= nvalid) off -= (ld_row[k] - (nvalid - 1)) * kRowBytes;  // repeat last row
-      if (ld_ok[k]) dma16(base + off, dst + (k * NW + wave) * 1024);
+      for (int k = 0; k < C::kMainCopies; ++k) dma16(base + ld_off[k], dst + (k * NW + wave) * 1024);
+      if (tail_lane) dma16(base + tail_off, dst + C::kMainCopies * NW * 1024);
+    } else {  // last tile of a request: rows past its end repeat its last row
+#pragma unroll
+      for (int k = 0; k < C::kMainCopies; ++k) {
+        const int row = ld_row[k] < nvalid ? ld_row[k] : nvalid - 1;
+        dma16(base + ld_off[k] - (ld_row[k] - row) * kRowBytes, dst + (k * NW + wave) * 1024);
+      }
+      const int row = tail_row < nvalid ? tail_row : nvalid - 1;
+      if (tail_lane) dma16(base + tail_off - (tail_row - row) * kRowBytes, dst + C::kMainCopies * NW * 1024);
     }
   };
 
@@ -193,12 +223,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   };
 
   // prologue: up to kStages-1 tiles in flight
-  int64_t issued = 0;
+  int issued = 0;
 #pragma unroll
   for (int s = 0; s < kStages - 1; ++s) {
     if (issued < total) {
       issue(s);
-      if (++issued < total) cursor_next(lc, p.part);
+      if (++issued < total) cursor_next(lc, p, tpp);
     }
   }
   load_q(cc.b);
@@ -208,26 +238,36 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   for (int m = 0; m < kVTiles; ++m) oacc[m] = f32x4{};
   float m_run = -INFINITY;
   float l_run = 0.f;
-  int64_t piece_t0 = cc.t;  // first tile of the current piece inside request cc.b
+  int piece_t0 = cc.t;  // first tile of the current piece inside request cc.b
   bool first_piece = true;
+  int cstage = 0, istage = kStages - 1;
 
-  for (int64_t i = 0; i < total; ++i) {
-    wait_tile_wave<NW>(wave, issued - 1 - i);
+  for (int i = 0; i < total; ++i) {
+    // Tile i has landed once at most the copies of the kStages-2 tiles issued after
+    // it are outstanding (younger memory operations only make the wait stricter);
+    // near the end of the span, drain everything.
+    if (issued - i == kStages - 1) {
+      if (extra_copy) wait_vmcnt_builtin<C::kLoadsMax * (kStages - 2)>();
+      else wait_vmcnt_builtin<C::kLoadsMin * (kStages - 2)>();
+    } else {
+      wait_vmcnt_builtin<0>();
+    }
     wg_barrier();
     if (issued < total) {
-      issue((int)(issued % kStages));
-      if (++issued < total) cursor_next(lc, p.part);
+      issue(istage);
+      istage = istage + 1 == kStages ? 0 : istage + 1;
+      if (++issued < total) cursor_next(lc, p, tpp);
     }
 
-    const DCP_LDS uint8_t* tb = lds + (int)(i % kStages) * kTileBytes;
-    const int64_t tok0 = cc.t * kTile;
-    const int nvalid = (int)((cc.Lr - tok0) < kTile ? (cc.Lr - tok0) : kTile);
+    const DCP_LDS uint8_t* tb = lds + cstage * kTileBytes;
+    cstage = cstage + 1 == kStages ? 0 : cstage + 1;
+    const int nvalid = cc.Lr - cc.t * kTile;   // >= kTile for every tile but a request's last
 
     // ---- S^T [32 tokens x 16 heads] = K [32 x 576] Q^T, as two 16-token chains.
     // Operand reads run kPrefetch k-steps ahead of the MFMAs.
     f32x4 s0 = f32x4{}, s1 = f32x4{};
     {
-      const DCP_LDS uint8_t* ka = tb + chunk_off(l16, q4);   // + 64 * s (+ 16 rows)
+      const DCP_LDS uint8_t* ka = tb + chunk_off(tile_row(l16), q4);   // + 64 * s (+ 16 rows)
       bf16x8 r0[kPrefetch], r1[kPrefetch];
 #pragma unroll
       for (int s = 0; s < kPrefetch; ++s) {
@@ -255,18 +295,18 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPrefetch, 0);
     }
 
-    // ---- online softmax (base 2).  Lane: head l16, tokens 16*(j/4) + 4*q4 + j%4.
+    // ---- online softmax (base 2).  Lane: head l16, tokens 16*(j/4) + tile_row(4*q4 + j%4).
     float x[8];
-    float mloc = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 16 * (j >> 2) + 4 * q4 + (j & 3);
-      const float sv = j < 4 ? s0[j] : s1[j - 4];
-      x[j] = tok < nvalid ? sv * p.scale_log2 : -INFINITY;
-      mloc = fmaxf(mloc, x[j]);
+    for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? s0[j] : s1[j - 4]) * p.scale_log2;
+    if (nvalid < kTile) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (16 * (j >> 2) + tile_row(4 * q4 + (j & 3)) >= nvalid) x[j] = -INFINITY;
     }
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-    mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+    float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mloc = max_over_groups(mloc);
     const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
     const float alpha = fast_exp2(m_run - m_new);
     float lsum = 0.f;
@@ -277,8 +317,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
       lsum += pr;
       pb[j] = (__bf16)pr;
     }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
+    lsum = sum_over_groups(lsum);
     l_run = l_run * alpha + lsum;
     if (__any(m_new != m_run)) {
 #pragma unroll
@@ -287,10 +326,12 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
     m_run = m_new;
 
     // ---- O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] P^T [32 x 16].
-    // Source lane l16 of each 16-lane group addresses row 4*q4 + l16/4 (and +16),
-    // dims 16m + 4*(l16%4) .. +3, i.e. chunk 2m + (l16%4)/2, half (l16%2).
+    // Source lane l16 of each 16-lane group addresses row tile_row(4*q4 + l16/4) (and
+    // +16), dims 16m + 4*(l16%4) .. +3, i.e. chunk 2m + (l16%4)/2, half (l16%2); lane
+    // i then holds dim 16m + i of the tokens P's element j stands for.
     {
-      const DCP_LDS uint8_t* va = tb + chunk_off(4 * q4 + (l16 >> 2), (l16 & 3) >> 1) + (l16 & 1) * 8;
+      const DCP_LDS uint8_t* va =
+          tb + chunk_off(tile_row(4 * q4 + (l16 >> 2)), (l16 & 3) >> 1) + (l16 & 1) * 8;
       u32x2 v1[kPrefetch], v2[kPrefetch];
 #pragma unroll
       for (int m = 0; m < kPrefetch; ++m) {
@@ -333,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
         }
       }
       if (i + 1 < total) {
-        cursor_next(cc, p.part);
+        cursor_next(cc, p, tpp);
         piece_t0 = 0;
         first_piece = false;
         load_q(cc.b);
@@ -344,7 +385,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
         l_run = 0.f;
       }
     } else {
-      cursor_next(cc, p.part);
+      cursor_next(cc, p, tpp);
     }
   }
 }
