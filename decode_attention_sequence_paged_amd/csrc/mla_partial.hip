@@ -187,8 +187,15 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   cursor_set(lc, p, tpp, loc.b0, (int)loc.off0);
   cc = lc;
 
+  // The page id is fetched (a scalar load the wave must wait for) only when the
+  // loader enters a new page, i.e. once per tpp tiles.
+  int32_t page = 0;
+  bool page_stale = true;
   auto issue = [&](int stage) {
-    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    if (lc.sub == 0 || page_stale) {
+      page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+      page_stale = false;
+    }
     const uint8_t* base = p.k_cache + page * page_bytes + lc.sub * (kTile * kRowBytes);
     DCP_LDS uint8_t* dst = lds + stage * kTileBytes;
     const int nvalid = lc.Lr - lc.t * kTile;
