@@ -7,21 +7,31 @@
 // the latent space).  Output: normalised partial O [B,H,512] and LSE [B,H].
 //
 // Design for gfx950:
-//  * A work-group owns up to 64 query heads (4 waves x 16 heads) and a
-//    token-balanced span of the rank's 32-token tiles; the span may cover the end
-//    of one request, whole requests and the start of another.  Every latent row is
-//    read from HBM once per head group and serves as both K and V.
+//  * A work-group owns up to 64 query heads and a token-balanced span of the rank's
+//    32-token tiles; the span may cover the end of one request, whole requests and
+//    the start of another.  Every latent row is read from HBM once per head group
+//    and serves as both K and V.
 //  * Tiles stream HBM -> LDS through a 4-stage ring of 16-byte direct-to-LDS copies
-//    (no VGPR staging), issued three tiles ahead and continuing across request
-//    boundaries.  LDS rows are padded to an odd stride of 73 16-byte slots, which
-//    keeps the 16-row MFMA operand reads free of bank conflicts with affine
-//    addresses; operand reads are software-pipelined a few MFMA steps ahead.
-//  * Each wave owns 16 heads over the full 576 dims, so waves never exchange
-//    partial scores: S^T = K Q^T (two 16x16x32 bf16 MFMA chains, tokens on the
-//    rows, heads on the columns; the wave's 16 x 576 q slice lives in VGPRs), then
-//    base-2 online softmax whose statistics are lane-local per head, then
-//    O^T += V^T P^T where the S^T accumulator converted to bf16 is the B operand
-//    and V^T comes from LDS through the transposing ds_read_b64_tr_b16.
+//    (no VGPR staging).  A tile is 32 rows of 72 16-byte slots; inside each row the
+//    chunks are XOR-swizzled in groups of 8, which makes both operand read patterns
+//    (16 rows x one chunk for K, 8 rows x 32 bytes for the transposed V reads) free
+//    of LDS bank conflicts while a tile stays exactly 36 copy instructions.
+//  * The work-group is a grid of waves: head halves (32 heads each) x token halves.
+//    A wave computes the scores of its 32 heads against its 16 tokens of the tile
+//    (S^T = K Q^T, 16x16x32 bf16 MFMA, tokens on the rows; one K operand read feeds
+//    both 16-head blocks) and publishes them in LDS; both waves of a head half then
+//    hold all 32 scores of their heads and run the same base-2 online softmax, and
+//    each accumulates its half (256 dims) of O^T += V^T P^T, V^T coming from LDS
+//    through the transposing ds_read_b64_tr_b16.  Each K or V byte of the tile is
+//    read from LDS by two waves rather than by every wave.  The wave's 32 x 576
+//    query slice lives in accumulation registers.
+//  * The copies of tile i+3 are spread between the P.V MFMAs of tile i, so their
+//    issue (which stalls while the memory pipeline is full) hides under the matrix
+//    pipe.  Copy issue has no branches: past the end of the span the last tile is
+//    copied again into a stage nobody reads.
+//  * Rows of a request's last, partial tile past its end are copied from the page
+//    like any other row (they stay inside the page) and are made inert: their scores
+//    are set to -inf and their V part is zeroed in LDS before it is read.
 //  * The running maximum moves only when a tile's maximum exceeds it by more than
 //    kRescaleSlack (log2 units), so the 128-register O accumulator is rarely
 //    rescaled; P stays <= 2^kRescaleSlack and the final LSE uses the same maximum,
@@ -37,47 +47,35 @@ constexpr int kDv = 512;
 constexpr int kRowBytes = kDqk * 2;            // 1152
 constexpr int kChunks = kRowBytes / 16;        // 72 16-byte chunks per row
 constexpr int kTile = 32;                      // tokens per tile
-constexpr int kRowSlots = kChunks + 1;         // 73: odd LDS row stride in 16-byte slots
-constexpr int kLdsRowBytes = kRowSlots * 16;   // 1168
-constexpr int kTileSlots = kTile * kRowSlots;  // 2336
-constexpr int kTileBytes = kTileSlots * 16;    // 37376
+constexpr int kTileBytes = kTile * kRowBytes;  // 36864: LDS tile = global tile
+constexpr int kCopyInstr = kTileBytes / 1024;  // 36 wave-wide 16-byte copies per tile
 constexpr int kStages = 4;
-constexpr int kPrefetch = 4;                   // LDS operand reads issued this many steps ahead
 constexpr int kKSteps = kDqk / 32;             // 18 k-steps of 32 dims
-constexpr int kVTiles = kDv / 16;              // 32 O^T tiles of 16 dims
+constexpr int kVBlocks = kDv / 2 / 16;         // 16 O^T blocks of 16 dims per wave
+constexpr int kPrefetchK = 6;                  // K operand reads issued ahead of their MFMAs
+constexpr int kPrefetchV = 4;                  // V^T operand steps issued ahead
 constexpr float kRescaleSlack = 8.0f;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// LDS byte offset of 16-byte chunk c of tile row `row`.  Rows are kRowSlots = 73
-// slots apart: an odd stride puts the same chunk of 16 consecutive rows in 16
-// different 4-bank groups (no conflicts), while every operand address stays
-// affine in the chunk index (one base register plus an immediate offset).
-__device__ __forceinline__ constexpr int chunk_off(int row, int c) { return row * kLdsRowBytes + c * 16; }
+// XOR swizzle of the chunks of tile row r inside their aligned group of 8.  With a
+// row stride of 72 slots (8 mod 16), the 16-byte bank group of (r, c) is
+// 8*(r%2) + (c ^ x(r)) mod 16; x(r) = 2*((r>>1)&3) + ((r>>3)&1) gives
+//  * 16 distinct groups for rows 16a..16a+15 at one chunk (K operand reads), and
+//  * 8 distinct group pairs for rows 8b..8b+7 at one even/odd chunk pair (the
+//    transposed V reads serve 32 lanes = 8 rows x 32 bytes per LDS pass).
+__device__ __forceinline__ constexpr int row_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
 
-// Token (= LDS row) behind row i of a 16-row MFMA tile: rows 0..7 take the even
-// tokens, rows 8..15 the odd ones.  The transposing read of V serves 32 lanes per
-// LDS pass, i.e. lane groups q4 = {0,1} and {2,3}; with this order each pass reads 8
-// rows of one parity, whose 32-byte pieces fall into disjoint banks at the 73-slot
-// stride, and the 16 rows of an S^T tile stay distinct modulo 16 for the QK reads.
-__device__ __forceinline__ constexpr int tile_row(int i) { return i < 8 ? 2 * i : 2 * (i - 8) + 1; }
-
-template <int NW>
+// NH head halves of 32 heads per work-group; 2 * NH waves (token halves x head halves).
+template <int NH>
 struct Cfg {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kHeads = 16 * NW;
-  // A tile is kTileSlots 16-byte slots written 64 at a time (one DMA instruction of a
-  // wave); instruction j = k * NW + wave covers slots [64 j, 64 j + 64).  The slot
-  // count is not a multiple of 64 * NW, so wave 0 issues one more (partly masked)
-  // instruction than the others.
-  static constexpr int kInstr = (kTileSlots + 63) / 64;        // 37
-  static constexpr int kMainCopies = (kInstr - 1) / NW;        // full instructions per wave
-  static constexpr int kTailLanes = kTileSlots - (kInstr - 1) * 64;  // 32 lanes of the last one
-  static_assert((kInstr - 1) % NW == 0, "full copy instructions must split evenly over waves");
-  static constexpr int kLoadsMax = kMainCopies + 1;            // wave 0
-  static constexpr int kLoadsMin = kMainCopies;                // the other waves
-  static_assert(kLoadsMax * (kStages - 2) < 64, "vmcnt range");
+  static constexpr int kWaves = 2 * NH;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kHeads = 32 * NH;
+  static constexpr int kCopies = kCopyInstr / kWaves;  // copy instructions per wave per tile
+  static_assert(kCopyInstr % kWaves == 0, "copies must split evenly over waves");
+  static_assert(2 * kCopies < 64, "vmcnt range");
 };
 
 // Position in the span's sequence of (request, tile) pairs, 32-bit and division
@@ -128,16 +126,61 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p) {
-  using C = Cfg<NW>;
+// s_waitcnt lgkmcnt(0) as a builtin, so the compiler's own wait counting knows every
+// earlier LDS access and scalar load has completed.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ uint32_t lds_addr(const DCP_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Exchange of scores through LDS.  Written as asm: the compiler's wait counting
+// cannot tell the exchange buffer from the stages the in-flight direct-to-LDS copies
+// write, and would drain those copies before every access.  The read waits for its
+// own data; the writes are completed by the caller's wait before the barrier.
+// read_scores: the four 16-byte slots (token half h, head block hb) at 1024 (2h+hb).
+__device__ __forceinline__ void read_scores(uint32_t addr, f32x4 (&h0)[2], f32x4 (&h1)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\t"
+      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(h0[0]), "=v"(h0[1]), "=v"(h1[0]), "=v"(h1[1])
+      : "v"(addr)
+      : "memory");
+}
+__device__ __forceinline__ void write_scores(uint32_t addr, f32x4 a, f32x4 b) {
+  asm volatile(
+      "ds_write_b128 %0, %1\n\t"
+      "ds_write_b128 %0, %2 offset:1024"
+      :
+      : "v"(addr), "v"(a), "v"(b)
+      : "memory");
+}
+// 16-byte global -> LDS copy: lane i's bytes from base + off land at lds_dst + 16 i.
+// Also asm, for the same reason: the compiler then neither counts these copies nor
+// drains them before LDS accesses; the kernel's explicit vmcnt waits order them.
+// No memory clobber: the copies only write a stage that no access in flight
+// touches, so LDS reads may be scheduled freely around them.
+__device__ __forceinline__ void copy16(const uint8_t* base, uint32_t off, uint32_t lds_dst) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds_dst));
+}
+__device__ __forceinline__ void zero_lds16(uint32_t addr) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(u32x4{0u, 0u, 0u, 0u}) : "memory");
+}
+
+template <int NH>
+__global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams p) {
+  using C = Cfg<NH>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) f32x4 s_xch[NH * 2 * 2 * 64];  // [hh][half][hb][lane]
   __shared__ int64_t s_scan[C::kThreads];
   __shared__ int64_t s_loc[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  const int tt = wave & 1;          // token half of the scores, dim half of O
+  const int hh = wave >> 1;         // head half
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
 
@@ -151,250 +194,305 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_partial_kernel(PartialParams p
   const int total = (int)(loc.end - loc.start);
   const int tpp = p.block_size / kTile;                    // tiles per page
   const int64_t page_bytes = (int64_t)p.block_size * kRowBytes;
-  // DMA copy instructions this wave issues per tile (wave 0 has the extra one).
-  const bool extra_copy = wave == 0;
 
   const int H = p.num_q_heads;
-  const int head = hg * C::kHeads + wave * 16 + l16;  // this lane's head (S^T column)
-  const bool head_ok = head < H;
+  const int head0 = hg * C::kHeads + hh * 32 + l16;  // this lane's head in block 0 (+16: block 1)
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
-  // This lane's DMA copies: LDS slot (k * NW + wave) * 64 + lane of every tile
-  // holds chunk (slot % 73) of row (slot / 73).  The 73rd slot of a row is never
-  // read; its lane copies the row's last chunk again (same cache line) instead of
-  // branching.  Every wave issues kMainCopies full instructions; wave 0 adds the
-  // half-filled tail instruction, whose lanes past the tile are masked.
-  int ld_row[C::kMainCopies];
-  int ld_off[C::kMainCopies];
+  // This lane's copies: LDS slot s = (k * kWaves + wave) * 64 + lane of a tile is
+  // position s % 72 of row s / 72, which holds chunk (pos ^ row_swz(row)).
+  uint32_t ld_off[C::kCopies];
 #pragma unroll
-  for (int k = 0; k < C::kMainCopies; ++k) {
-    const int s = (k * NW + wave) * 64 + lane;
-    const int row = s / kRowSlots;
-    const int c = s - row * kRowSlots;
-    ld_row[k] = row;
-    ld_off[k] = row * kRowBytes + (c < kChunks ? c : kChunks - 1) * 16;
+  for (int k = 0; k < C::kCopies; ++k) {
+    const int s = (k * C::kWaves + wave) * 64 + lane;
+    const int row = s / kChunks;
+    const int pos = s - row * kChunks;
+    ld_off[k] = (uint32_t)(row * kRowBytes + (pos ^ row_swz(row)) * 16);
   }
-  int tail_row, tail_off;
+
+  // Operand read offsets inside a stage.  K: row 16 tt + l16, chunk 4 s + q4
+  // -> kb[s & 1] + 128 (s >> 1).  V: row 4 q4 + l16 / 4 (+16 rows for the second
+  // token half), dims 256 tt + 16 m + 4 (l16 % 4) .. +3, i.e. chunk
+  // 32 tt + 2 m + (l16 % 4) / 2, byte half l16 % 2 -> vb[m & 3] + 128 (m >> 2).
+  uint32_t kb[2], vb[4];
   {
-    const int s = C::kMainCopies * NW * 64 + lane;
-    tail_row = s / kRowSlots;
-    const int c = s - tail_row * kRowSlots;
-    tail_off = tail_row * kRowBytes + (c < kChunks ? c : kChunks - 1) * 16;
+    const int r = 16 * tt + l16;
+    const int x = row_swz(r);
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      kb[v] = (uint32_t)(r * kRowBytes + 64 * (v ^ (x >> 2)) + 16 * (q4 ^ (x & 3)));
   }
-  const bool tail_lane = wave == 0 && lane < C::kTailLanes;
+  {
+    const int r = 4 * q4 + (l16 >> 2);
+    const int x = row_swz(r);
+    const int h = (l16 & 3) >> 1;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      vb[v] = (uint32_t)(r * kRowBytes + 512 * tt + 32 * (v ^ (x >> 1)) + 16 * (h ^ (x & 1)) +
+                         8 * (l16 & 1));
+  }
 
   Cursor lc, cc;
   cursor_set(lc, p, tpp, loc.b0, (int)loc.off0);
   cc = lc;
 
-  // The page id is fetched (a scalar load the wave must wait for) only when the
-  // loader enters a new page, i.e. once per tpp tiles.
-  int32_t page = 0;
-  bool page_stale = true;
-  auto issue = [&](int stage) {
-    if (lc.sub == 0 || page_stale) {
-      page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
-      page_stale = false;
+  // Copy source: the tile the loader cursor is on.  Past the end of the span the
+  // cursor stays on the last tile, which is then copied again (into a stage no wave
+  // reads) so that the copy code in the loop needs no branch.
+  int lc_left = total;  // tiles the loader has not moved past yet
+  const uint8_t* src = nullptr;
+  auto next_src = [&]() {
+    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    src = p.k_cache + page * page_bytes + lc.sub * kTileBytes;
+  };
+  auto advance_loader = [&]() {
+    if (--lc_left > 0) {
+      cursor_next(lc, p, tpp);
+      next_src();
     }
-    const uint8_t* base = p.k_cache + page * page_bytes + lc.sub * (kTile * kRowBytes);
-    DCP_LDS uint8_t* dst = lds + stage * kTileBytes;
-    const int nvalid = lc.Lr - lc.t * kTile;
-    if (nvalid >= kTile) {
+  };
+  auto issue_copy = [&](int k, int stage) {
+    copy16(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * C::kWaves + wave) * 1024));
+  };
+
+  // q[b, head0 + 16 hb, 32 s + 8 q4 .. +7]: the B operand of S^T = K Q^T for head
+  // block hb and k-step s.  It is only an MFMA operand, so it is loaded straight
+  // into accumulation registers, leaving the VGPRs to the O accumulator and the
+  // operand prefetch rings.  Lanes of heads past H load head 0's slice: their
+  // score columns are independent of the others and never stored.  The loads are
+  // not tracked by the compiler's wait counting; the loop's explicit vmcnt waits
+  // cover them (memory clobber: they stay in program order with the tile copies).
+  bf16x8 qreg[2][kKSteps];
+  auto load_q = [&](int b) {
 #pragma unroll
-      for (int k = 0; k < C::kMainCopies; ++k) dma16(base + ld_off[k], dst + (k * NW + wave) * 1024);
-      if (tail_lane) dma16(base + tail_off, dst + C::kMainCopies * NW * 1024);
-    } else {  // last tile of a request: rows past its end repeat its last row
+    for (int hb = 0; hb < 2; ++hb) {
+      const int head = head0 + 16 * hb;
+      const uint16_t* qp = p.q + ((int64_t)b * H + (head < H ? head : 0)) * kDqk + 8 * q4;
 #pragma unroll
-      for (int k = 0; k < C::kMainCopies; ++k) {
-        const int row = ld_row[k] < nvalid ? ld_row[k] : nvalid - 1;
-        dma16(base + ld_off[k] - (ld_row[k] - row) * kRowBytes, dst + (k * NW + wave) * 1024);
-      }
-      const int row = tail_row < nvalid ? tail_row : nvalid - 1;
-      if (tail_lane) dma16(base + tail_off - (tail_row - row) * kRowBytes, dst + C::kMainCopies * NW * 1024);
+      for (int s = 0; s < kKSteps; ++s)
+        asm volatile("global_load_dwordx4 %0, %1, off offset:%2"
+                     : "=a"(qreg[hb][s]) : "v"(qp), "n"(64 * s) : "memory");
     }
   };
 
-  // q[b, head, 32*s + 8*q4 .. +7]: the B operand of S^T = K Q^T for k-step s.
-  bf16x8 qreg[kKSteps];
-  auto load_q = [&](int b) {
-    const uint16_t* qp = p.q + ((int64_t)b * H + (head_ok ? head : 0)) * kDqk + 8 * q4;
+  // S^T [16 tokens x 32 heads] for this wave's token half of the tile at `tb`: four
+  // accumulation chains (2 head blocks x even/odd k-steps); one K read feeds both
+  // head blocks.  The scores come back scaled to log2 units.
+  auto qk = [&](const DCP_LDS uint8_t* tb, f32x4& o0, f32x4& o1) {
+    f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+    bf16x8 r[kPrefetchK];
+#pragma unroll
+    for (int s = 0; s < kPrefetchK; ++s)
+      r[s] = *(const DCP_LDS bf16x8*)(tb + kb[s & 1] + 128 * (s >> 1));
 #pragma unroll
     for (int s = 0; s < kKSteps; ++s) {
-      bf16x8 v = *(const bf16x8*)(qp + 32 * s);
-      qreg[s] = head_ok ? v : bf16x8{};
+      const bf16x8 a = r[s % kPrefetchK];
+      const int sn = s + kPrefetchK;
+      if (sn < kKSteps) r[s % kPrefetchK] = *(const DCP_LDS bf16x8*)(tb + kb[sn & 1] + 128 * (sn >> 1));
+      sacc[0][s & 1] = mfma16x16x32(a, qreg[0][s], sacc[0][s & 1]);
+      sacc[1][s & 1] = mfma16x16x32(a, qreg[1][s], sacc[1][s & 1]);
     }
-    // The q slice is only an MFMA operand: keep it in accumulation registers so the
-    // VGPRs stay free for the O accumulator and the operand prefetch ring.
+    // Keep kPrefetchK operand reads in flight: reads first, then (2 MFMA, 1 read) ...
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetchK, 0);
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) asm volatile("" : "+a"(qreg[s]));
+    for (int s = 0; s < kKSteps - kPrefetchK; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPrefetchK, 0);
+    o0 = (sacc[0][0] + sacc[0][1]) * p.scale_log2;
+    o1 = (sacc[1][0] + sacc[1][1]) * p.scale_log2;
   };
 
-  // prologue: up to kStages-1 tiles in flight
-  int issued = 0;
+  // Running softmax state of the tile whose P.V is next: per head block, the
+  // maximum (log2 units), the sum, and P^T of the tile as the B operand.
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  bf16x8 pb[2];
+  float alpha[2];
+  bool moved = false;
+  // Softmax over the 32 scores per head (elements 0..3: first token half, rows
+  // 4 q4 + j; 4..7: second half).  Both waves of a head half evaluate it on the
+  // same values in the same order and so agree bit for bit.
+  auto softmax = [&](const f32x4 (&h0)[2], const f32x4 (&h1)[2]) {
+    moved = false;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (issued < total) {
-      issue(s);
-      if (++issued < total) cursor_next(lc, p, tpp);
+    for (int hb = 0; hb < 2; ++hb) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { x[j] = h0[hb][j]; x[j + 4] = h1[hb][j]; }
+      float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mloc = max_over_groups(mloc);
+      const float m_new = mloc > m_run[hb] + kRescaleSlack ? mloc : m_run[hb];
+      alpha[hb] = fast_exp2(m_run[hb] - m_new);
+      moved |= m_new != m_run[hb];
+      float lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pr = fast_exp2(x[j] - m_new);
+        lsum += pr;
+        pb[hb][j] = (__bf16)pr;
+      }
+      lsum = sum_over_groups(lsum);
+      l_run[hb] = l_run[hb] * alpha[hb] + lsum;
+      m_run[hb] = m_new;
     }
-  }
-  load_q(cc.b);
+  };
 
-  f32x4 oacc[kVTiles];
+  f32x4 oacc[2][kVBlocks];
 #pragma unroll
-  for (int m = 0; m < kVTiles; ++m) oacc[m] = f32x4{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  int piece_t0 = cc.t;  // first tile of the current piece inside request cc.b
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] = f32x4{};
+
+  // O^T [256 dims x 32 heads] += V^T [256 x 32 tokens] P^T [32 x 32] for the tile at
+  // `tb`, with this wave's copies of a later tile (into `stage`) spread between the
+  // MFMAs: the copy asm orders itself with the LDS reads around it, so its place in
+  // the source is its place in the instruction stream.  Source lane l16 of each
+  // 16-lane group addresses row 4 q4 + l16 / 4 (and +16); lane i then holds dim
+  // 16 m + i of the tokens P's element j stands for.
+  auto pv = [&](const DCP_LDS uint8_t* tb, int stage) {
+    u32x2 v1[kPrefetchV], v2[kPrefetchV];
+#pragma unroll
+    for (int m = 0; m < kPrefetchV; ++m) {
+      v1[m] = lds_read_tr16(tb + vb[m & 3] + 128 * (m >> 2));
+      v2[m] = lds_read_tr16(tb + vb[m & 3] + 128 * (m >> 2) + 16 * kRowBytes);
+    }
+#pragma unroll
+    for (int m = 0; m < kVBlocks; ++m) {
+      const bf16x8 a = join_tr16(v1[m % kPrefetchV], v2[m % kPrefetchV]);
+      const int mn = m + kPrefetchV;
+      if (mn < kVBlocks) {
+        v1[m % kPrefetchV] = lds_read_tr16(tb + vb[mn & 3] + 128 * (mn >> 2));
+        v2[m % kPrefetchV] = lds_read_tr16(tb + vb[mn & 3] + 128 * (mn >> 2) + 16 * kRowBytes);
+      }
+#pragma unroll
+      for (int k = 0; k < C::kCopies; ++k)
+        if (k * kVBlocks / C::kCopies == m) issue_copy(k, stage);
+      oacc[0][m] = mfma16x16x32(a, pb[0], oacc[0][m]);
+      oacc[1][m] = mfma16x16x32(a, pb[1], oacc[1][m]);
+    }
+  };
+
+  // Zero the V part (chunks 0..63 = positions 0..63: the swizzle keeps groups of 8)
+  // of rows nvalid..31 of the tile at `tb`.
+  auto zero_tail = [&](const DCP_LDS uint8_t* tb, int nvalid) {
+    const int n = (kTile - nvalid) * 64;
+    for (int e = tid; e < n; e += C::kThreads)
+      zero_lds16(lds_addr(tb + (nvalid + (e >> 6)) * kRowBytes + (e & 63) * 16));
+  };
+
+  // Mask the scores of tokens past the end (rows 16 tt + 4 q4 + j of the tile).
+  auto mask_scores = [&](f32x4& o0, f32x4& o1, int nvalid) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (16 * tt + 4 * q4 + j >= nvalid) o0[j] = o1[j] = -INFINITY;
+  };
+
+  const uint32_t xch_own = lds_addr((const DCP_LDS f32x4*)s_xch + (hh * 4 + tt * 2) * 64 + lane);
+  const uint32_t xch_half = lds_addr((const DCP_LDS f32x4*)s_xch + hh * 4 * 64 + lane);
+
+  // ---- prologue: query slice, then three tiles in flight
+  load_q(cc.b);
+  next_src();
+  for (int s = 0; s < kStages - 1; ++s) {
+#pragma unroll
+    for (int k = 0; k < C::kCopies; ++k) issue_copy(k, s);
+    advance_loader();
+  }
+  int issued = kStages - 1;  // copy rounds issued (the last ones may repeat a tile)
+  int q_after = 0;           // copy rounds issued before the newest query load
+  int piece_t0 = cc.t;       // first tile of the current piece inside request cc.b
   bool first_piece = true;
-  int cstage = 0, istage = kStages - 1;
 
   for (int i = 0; i < total; ++i) {
-    // Tile i has landed once at most the copies of the kStages-2 tiles issued after
-    // it are outstanding (younger memory operations only make the wait stricter);
-    // near the end of the span, drain everything.
-    if (issued - i == kStages - 1) {
-      if (extra_copy) wait_vmcnt_builtin<C::kLoadsMax * (kStages - 2)>();
-      else wait_vmcnt_builtin<C::kLoadsMin * (kStages - 2)>();
-    } else {
-      wait_vmcnt_builtin<0>();
+    // Tile i (and the newest query slice) have landed once only the copy rounds
+    // issued after both are outstanding; younger memory operations only make the
+    // wait stricter.  The barrier then also guarantees every wave has finished the
+    // P.V of tile i-1, whose stage this iteration's copies refill.
+    {
+      const int after_tile = issued - (i + 1);
+      const int after_q = issued - q_after;
+      const int after = after_tile < after_q ? after_tile : after_q;
+      if (after >= 2) wait_vmcnt_builtin<2 * C::kCopies>();
+      else if (after == 1) wait_vmcnt_builtin<C::kCopies>();
+      else wait_vmcnt_builtin<0>();
     }
     wg_barrier();
-    if (issued < total) {
-      issue(istage);
-      istage = istage + 1 == kStages ? 0 : istage + 1;
-      if (++issued < total) cursor_next(lc, p, tpp);
+    // The loader's scalar loads were issued an iteration ago; retiring them here
+    // lets the operand reads below wait for single LDS accesses, not for lgkmcnt(0).
+    wait_lgkm();
+    const DCP_LDS uint8_t* tb = lds + (i % kStages) * kTileBytes;
+    const Cursor cur = cc;
+    const int nvalid = cur.Lr - cur.t * kTile;  // >= kTile for every tile but a request's last
+    if (nvalid < kTile) zero_tail(tb, nvalid);
+
+    f32x4 o0, o1;
+    qk(tb, o0, o1);
+    if (nvalid < kTile) mask_scores(o0, o1, nvalid);
+    // The next request's query slice as soon as this one's last scores are done,
+    // ahead of the copies issued below.
+    if (i + 1 < total) {
+      cursor_next(cc, p, tpp);
+      if (cc.b != cur.b) {
+        load_q(cc.b);
+        q_after = issued;
+      }
     }
-
-    const DCP_LDS uint8_t* tb = lds + cstage * kTileBytes;
-    cstage = cstage + 1 == kStages ? 0 : cstage + 1;
-    const int nvalid = cc.Lr - cc.t * kTile;   // >= kTile for every tile but a request's last
-
-    // ---- S^T [32 tokens x 16 heads] = K [32 x 576] Q^T, as two 16-token chains.
-    // Operand reads run kPrefetch k-steps ahead of the MFMAs.
-    f32x4 s0 = f32x4{}, s1 = f32x4{};
+    write_scores(xch_own, o0, o1);
+    wait_lgkm();
+    wg_barrier();
     {
-      const DCP_LDS uint8_t* ka = tb + chunk_off(tile_row(l16), q4);   // + 64 * s (+ 16 rows)
-      bf16x8 r0[kPrefetch], r1[kPrefetch];
-#pragma unroll
-      for (int s = 0; s < kPrefetch; ++s) {
-        r0[s] = *(const DCP_LDS bf16x8*)(ka + 64 * s);
-        r1[s] = *(const DCP_LDS bf16x8*)(ka + 16 * kLdsRowBytes + 64 * s);
-      }
-#pragma unroll
-      for (int s = 0; s < kKSteps; ++s) {
-        const bf16x8 a0 = r0[s % kPrefetch];
-        const bf16x8 a1 = r1[s % kPrefetch];
-        if (s + kPrefetch < kKSteps) {
-          r0[s % kPrefetch] = *(const DCP_LDS bf16x8*)(ka + 64 * (s + kPrefetch));
-          r1[s % kPrefetch] = *(const DCP_LDS bf16x8*)(ka + 16 * kLdsRowBytes + 64 * (s + kPrefetch));
-        }
-        s0 = mfma16x16x32(a0, qreg[s], s0);
-        s1 = mfma16x16x32(a1, qreg[s], s1);
-      }
-      // Keep 2*kPrefetch operand reads in flight: reads first, then (2 MFMA, 2 reads) ...
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetch, 0);
-#pragma unroll
-      for (int s = 0; s < kKSteps - kPrefetch; ++s) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPrefetch, 0);
+      f32x4 h0[2], h1[2];
+      read_scores(xch_half, h0, h1);
+      softmax(h0, h1);
     }
+    if (__any(moved)) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] *= alpha[hb];
+    }
+    pv(tb, issued % kStages);
+    ++issued;
 
-    // ---- online softmax (base 2).  Lane: head l16, tokens 16*(j/4) + tile_row(4*q4 + j%4).
-    float x[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = (j < 4 ? s0[j] : s1[j - 4]) * p.scale_log2;
-    if (nvalid < kTile) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (16 * (j >> 2) + tile_row(4 * q4 + (j & 3)) >= nvalid) x[j] = -INFINITY;
-    }
-    float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    mloc = max_over_groups(mloc);
-    const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    float lsum = 0.f;
-    bf16x8 pb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float pr = fast_exp2(x[j] - m_new);
-      lsum += pr;
-      pb[j] = (__bf16)pr;
-    }
-    lsum = sum_over_groups(lsum);
-    l_run = l_run * alpha + lsum;
-    if (__any(m_new != m_run)) {
-#pragma unroll
-      for (int m = 0; m < kVTiles; ++m) oacc[m] *= alpha;
-    }
-    m_run = m_new;
-
-    // ---- O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] P^T [32 x 16].
-    // Source lane l16 of each 16-lane group addresses row tile_row(4*q4 + l16/4) (and
-    // +16), dims 16m + 4*(l16%4) .. +3, i.e. chunk 2m + (l16%4)/2, half (l16%2); lane
-    // i then holds dim 16m + i of the tokens P's element j stands for.
-    {
-      const DCP_LDS uint8_t* va =
-          tb + chunk_off(tile_row(4 * q4 + (l16 >> 2)), (l16 & 3) >> 1) + (l16 & 1) * 8;
-      u32x2 v1[kPrefetch], v2[kPrefetch];
-#pragma unroll
-      for (int m = 0; m < kPrefetch; ++m) {
-        v1[m] = lds_read_tr16(va + 32 * m);
-        v2[m] = lds_read_tr16(va + 16 * kLdsRowBytes + 32 * m);
-      }
-#pragma unroll
-      for (int m = 0; m < kVTiles; ++m) {
-        const bf16x8 a = join_tr16(v1[m % kPrefetch], v2[m % kPrefetch]);
-        if (m + kPrefetch < kVTiles) {
-          v1[m % kPrefetch] = lds_read_tr16(va + 32 * (m + kPrefetch));
-          v2[m % kPrefetch] = lds_read_tr16(va + 16 * kLdsRowBytes + 32 * (m + kPrefetch));
-        }
-        oacc[m] = mfma16x16x32(a, pb, oacc[m]);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetch, 1);
-#pragma unroll
-      for (int m = 0; m < kVTiles - kPrefetch; ++m) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 1);
-    }
-
-    // ---- end of a request piece: normalise and store, then move to the next request
-    const bool last_of_req = cc.t == cc.ntile - 1;
+    // ---- end of a request piece: normalise and store, then start the next request
+    const bool last_of_req = cur.t == cur.ntile - 1;
     if (last_of_req || i == total - 1) {
       const bool whole = piece_t0 == 0 && last_of_req;
-      if (head_ok) {
-        const float inv = 1.0f / l_run;
-        const int64_t slot = 2 * w + (first_piece ? 0 : 1);
-        float* orow = whole ? p.out_o + ((int64_t)cc.b * H + head) * kDv
-                            : p.ws_o + (slot * H + head) * kDv;
+      const int64_t slot = 2 * w + (first_piece ? 0 : 1);
 #pragma unroll
-        for (int m = 0; m < kVTiles; ++m) *(f32x4*)(orow + 16 * m + 4 * q4) = oacc[m] * inv;
-        if (q4 == 0) {
-          const float lse = (m_run + fast_log2(l_run)) * kLn2;
-          if (whole) p.out_lse[(int64_t)cc.b * H + head] = lse;
-          else p.ws_lse[slot * H + head] = lse;
+      for (int hb = 0; hb < 2; ++hb) {
+        const int head = head0 + 16 * hb;
+        if (head < H) {
+          const float inv = 1.0f / l_run[hb];
+          float* orow = whole ? p.out_o + ((int64_t)cur.b * H + head) * kDv
+                              : p.ws_o + (slot * H + head) * kDv;
+          orow += 256 * tt + 4 * q4;
+#pragma unroll
+          for (int m = 0; m < kVBlocks; ++m) *(f32x4*)(orow + 16 * m) = oacc[hb][m] * inv;
+          if (tt == 0 && q4 == 0) {
+            const float lse = (m_run[hb] + fast_log2(l_run[hb])) * kLn2;
+            if (whole) p.out_lse[(int64_t)cur.b * H + head] = lse;
+            else p.ws_lse[slot * H + head] = lse;
+          }
         }
       }
-      if (i + 1 < total) {
-        cursor_next(cc, p, tpp);
-        piece_t0 = 0;
-        first_piece = false;
-        load_q(cc.b);
-        wait_vmcnt_builtin<0>();
+      piece_t0 = 0;
+      first_piece = false;
 #pragma unroll
-        for (int m = 0; m < kVTiles; ++m) oacc[m] = f32x4{};
-        m_run = -INFINITY;
-        l_run = 0.f;
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] = f32x4{};
+        m_run[hb] = -INFINITY;
+        l_run[hb] = 0.f;
       }
-    } else {
-      cursor_next(cc, p, tpp);
     }
+    advance_loader();
   }
+  // No copy may still be landing in this work-group's LDS when it exits.
+  wait_vmcnt_builtin<0>();
 }
 
 }  // namespace mla
@@ -404,9 +502,9 @@ int mla_heads_per_group(int num_q_heads) { return num_q_heads <= 32 ? 32 : 64; }
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;
   if (mla_heads_per_group(p.num_q_heads) == 32)
-    hipLaunchKernelGGL(mla::mla_partial_kernel<2>, dim3(grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(mla::mla_partial_kernel<1>, dim3(grid), dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(mla::mla_partial_kernel<4>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla::mla_partial_kernel<2>, dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
