@@ -16,15 +16,18 @@
 //    chunks are XOR-swizzled in groups of 8, which makes both operand read patterns
 //    (16 rows x one chunk for K, 8 rows x 32 bytes for the transposed V reads) free
 //    of LDS bank conflicts while a tile stays exactly 36 copy instructions.
-//  * The work-group is a grid of waves: head halves (32 heads each) x token halves.
-//    A wave computes the scores of its 32 heads against its 16 tokens of the tile
-//    (S^T = K Q^T, 16x16x32 bf16 MFMA, tokens on the rows; one K operand read feeds
-//    both 16-head blocks) and publishes them in LDS; both waves of a head half then
-//    hold all 32 scores of their heads and run the same base-2 online softmax, and
-//    each accumulates its half (256 dims) of O^T += V^T P^T, V^T coming from LDS
-//    through the transposing ds_read_b64_tr_b16.  Each K or V byte of the tile is
-//    read from LDS by two waves rather than by every wave.  The wave's 32 x 576
-//    query slice lives in accumulation registers.
+//  * The work-group is a grid of waves: head halves (32 heads each) x partners.  The
+//    two partners of a head half split the 576 score dims (even / odd 32-dim
+//    steps): each computes partial scores of its 32 heads against all 32 tokens of
+//    the tile (S^T = K Q^T, 16x16x32 bf16 MFMA, tokens on the rows; one K operand
+//    read feeds both 16-head blocks) and hands the partial of the other's head block
+//    over through LDS.  Each wave then owns 16 heads: it adds the two partials, runs
+//    the base-2 online softmax over the 32 tokens and accumulates O^T += V^T P^T for
+//    its heads over all 512 dims, V^T coming from LDS through the transposing
+//    ds_read_b64_tr_b16.  K is read from LDS by two waves rather than by every wave,
+//    and no softmax is evaluated twice.  The wave's 32 x 288 query slice and its
+//    16 x 512 O accumulator live in accumulation registers (AGPR-form MFMA), which
+//    leaves the VGPRs to deep operand prefetch.
 //  * The copies of tile i+3 are spread between the P.V MFMAs of tile i, so their
 //    issue (which stalls while the memory pipeline is full) hides under the matrix
 //    pipe.  Copy issue has no branches: past the end of the span the last tile is
@@ -51,9 +54,10 @@ constexpr int kTileBytes = kTile * kRowBytes;  // 36864: LDS tile = global tile
 constexpr int kCopyInstr = kTileBytes / 1024;  // 36 wave-wide 16-byte copies per tile
 constexpr int kStages = 4;
 constexpr int kKSteps = kDqk / 32;             // 18 k-steps of 32 dims
-constexpr int kVBlocks = kDv / 2 / 16;         // 16 O^T blocks of 16 dims per wave
-constexpr int kPrefetchK = 6;                  // K operand reads issued ahead of their MFMAs
-constexpr int kPrefetchV = 4;                  // V^T operand steps issued ahead
+constexpr int kKStepsWave = kKSteps / 2;       // 9 per partner (even / odd steps)
+constexpr int kVBlocks = kDv / 16;             // 32 O^T blocks of 16 dims
+constexpr int kPrefetchK = 3;                  // K operand steps (2 reads each) issued ahead
+constexpr int kPrefetchV = 8;                  // V^T operand steps (2 reads each) issued ahead
 constexpr float kRescaleSlack = 8.0f;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
@@ -67,7 +71,7 @@ constexpr int kSchedDsRead = 0x100;
 //    transposed V reads serve 32 lanes = 8 rows x 32 bytes per LDS pass).
 __device__ __forceinline__ constexpr int row_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
 
-// NH head halves of 32 heads per work-group; 2 * NH waves (token halves x head halves).
+// NH head halves of 32 heads per work-group; 2 * NH waves (head halves x partners).
 template <int NH>
 struct Cfg {
   static constexpr int kWaves = 2 * NH;
@@ -132,19 +136,17 @@ __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F)
 
 __device__ __forceinline__ uint32_t lds_addr(const DCP_LDS void* p) { return (uint32_t)(uintptr_t)p; }
 
-// Exchange of scores through LDS.  Written as asm: the compiler's wait counting
-// cannot tell the exchange buffer from the stages the in-flight direct-to-LDS copies
-// write, and would drain those copies before every access.  The read waits for its
-// own data; the writes are completed by the caller's wait before the barrier.
-// read_scores: the four 16-byte slots (token half h, head block hb) at 1024 (2h+hb).
-__device__ __forceinline__ void read_scores(uint32_t addr, f32x4 (&h0)[2], f32x4 (&h1)[2]) {
+// Exchange of partial scores through LDS.  Written as asm: the compiler's wait
+// counting cannot tell the exchange buffer from the stages the in-flight
+// direct-to-LDS copies write, and would drain those copies before every access.
+// The read waits for its own data; the writes are completed by the caller's wait
+// before the barrier.  Two 16-byte slots, 1024 bytes apart (token blocks 0 and 1).
+__device__ __forceinline__ void read_scores(uint32_t addr, f32x4& a, f32x4& b) {
   asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %4 offset:1024\n\t"
-      "ds_read_b128 %2, %4 offset:2048\n\t"
-      "ds_read_b128 %3, %4 offset:3072\n\t"
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %2 offset:1024\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(h0[0]), "=v"(h0[1]), "=v"(h1[0]), "=v"(h1[1])
+      : "=v"(a), "=v"(b)
       : "v"(addr)
       : "memory");
 }
@@ -172,14 +174,14 @@ template <int NH>
 __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams p) {
   using C = Cfg<NH>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
-  __shared__ __attribute__((aligned(16))) f32x4 s_xch[NH * 2 * 2 * 64];  // [hh][half][hb][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 s_xch[NH * 2 * 2 * 64];  // [hh][writer kk][token block][lane]
   __shared__ int64_t s_scan[C::kThreads];
   __shared__ int64_t s_loc[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const int tt = wave & 1;          // token half of the scores, dim half of O
+  const int kk = wave & 1;          // score dims of k-steps 2 s + kk; head block of its softmax and O
   const int hh = wave >> 1;         // head half
   const int l16 = lane & 15;
   const int q4 = lane >> 4;
@@ -196,7 +198,8 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   const int64_t page_bytes = (int64_t)p.block_size * kRowBytes;
 
   const int H = p.num_q_heads;
-  const int head0 = hg * C::kHeads + hh * 32 + l16;  // this lane's head in block 0 (+16: block 1)
+  const int head0 = hg * C::kHeads + hh * 32 + l16;  // this lane's score column in head block 0 (+16: 1)
+  const int head = head0 + 16 * kk;                  // this lane's head for softmax and O
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
   // This lane's copies: LDS slot s = (k * kWaves + wave) * 64 + lane of a tile is
@@ -210,17 +213,16 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     ld_off[k] = (uint32_t)(row * kRowBytes + (pos ^ row_swz(row)) * 16);
   }
 
-  // Operand read offsets inside a stage.  K: row 16 tt + l16, chunk 4 s + q4
-  // -> kb[s & 1] + 128 (s >> 1).  V: row 4 q4 + l16 / 4 (+16 rows for the second
-  // token half), dims 256 tt + 16 m + 4 (l16 % 4) .. +3, i.e. chunk
-  // 32 tt + 2 m + (l16 % 4) / 2, byte half l16 % 2 -> vb[m & 3] + 128 (m >> 2).
+  // Operand read offsets inside a stage.  K: token block tb, row 16 tb + l16, chunk
+  // 4 s + q4 of k-step s = 2 s' + kk -> kb[tb] + 128 s'.  V: row 4 q4 + l16 / 4 (+16
+  // rows for the second token block), dims 16 m + 4 (l16 % 4) .. +3, i.e. chunk
+  // 2 m + (l16 % 4) / 2, byte half l16 % 2 -> vb[m & 3] + 128 (m >> 2).
   uint32_t kb[2], vb[4];
-  {
-    const int r = 16 * tt + l16;
-    const int x = row_swz(r);
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
-      kb[v] = (uint32_t)(r * kRowBytes + 64 * (v ^ (x >> 2)) + 16 * (q4 ^ (x & 3)));
+  for (int tb = 0; tb < 2; ++tb) {
+    const int r = 16 * tb + l16;
+    const int x = row_swz(r);
+    kb[tb] = (uint32_t)(r * kRowBytes + 64 * (kk ^ (x >> 2)) + 16 * (q4 ^ (x & 3)));
   }
   {
     const int r = 4 * q4 + (l16 >> 2);
@@ -228,8 +230,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     const int h = (l16 & 3) >> 1;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      vb[v] = (uint32_t)(r * kRowBytes + 512 * tt + 32 * (v ^ (x >> 1)) + 16 * (h ^ (x & 1)) +
-                         8 * (l16 & 1));
+      vb[v] = (uint32_t)(r * kRowBytes + 32 * (v ^ (x >> 1)) + 16 * (h ^ (x & 1)) + 8 * (l16 & 1));
   }
 
   Cursor lc, cc;
@@ -255,98 +256,98 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     copy16(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * C::kWaves + wave) * 1024));
   };
 
-  // q[b, head0 + 16 hb, 32 s + 8 q4 .. +7]: the B operand of S^T = K Q^T for head
-  // block hb and k-step s.  It is only an MFMA operand, so it is loaded straight
-  // into accumulation registers, leaving the VGPRs to the O accumulator and the
-  // operand prefetch rings.  Lanes of heads past H load head 0's slice: their
-  // score columns are independent of the others and never stored.  The loads are
-  // not tracked by the compiler's wait counting; the loop's explicit vmcnt waits
-  // cover them (memory clobber: they stay in program order with the tile copies).
-  bf16x8 qreg[2][kKSteps];
+  // q[b, head0 + 16 hb, 32 (2 s' + kk) + 8 q4 .. +7]: the B operand of S^T = K Q^T
+  // for head block hb and this wave's k-step s'.  It is only an MFMA operand, so it
+  // is loaded straight into accumulation registers.  Lanes of heads past H load
+  // head 0's slice: their score columns are independent of the others and never
+  // stored.  The loads are not tracked by the compiler's wait counting; the loop's
+  // explicit vmcnt waits cover them (memory clobber: they stay in program order
+  // with the tile copies).
+  bf16x8 qreg[2][kKStepsWave];
   auto load_q = [&](int b) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      const int head = head0 + 16 * hb;
-      const uint16_t* qp = p.q + ((int64_t)b * H + (head < H ? head : 0)) * kDqk + 8 * q4;
+      const int hd = head0 + 16 * hb;
+      const uint16_t* qp = p.q + ((int64_t)b * H + (hd < H ? hd : 0)) * kDqk + 32 * kk + 8 * q4;
 #pragma unroll
-      for (int s = 0; s < kKSteps; ++s)
+      for (int s = 0; s < kKStepsWave; ++s)
         asm volatile("global_load_dwordx4 %0, %1, off offset:%2"
-                     : "=a"(qreg[hb][s]) : "v"(qp), "n"(64 * s) : "memory");
+                     : "=a"(qreg[hb][s]) : "v"(qp), "n"(128 * s) : "memory");
     }
   };
 
-  // S^T [16 tokens x 32 heads] for this wave's token half of the tile at `tb`: four
-  // accumulation chains (2 head blocks x even/odd k-steps); one K read feeds both
-  // head blocks.  The scores come back scaled to log2 units.
-  auto qk = [&](const DCP_LDS uint8_t* tb, f32x4& o0, f32x4& o1) {
-    f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-    bf16x8 r[kPrefetchK];
+  // Partial S^T [32 tokens x 32 heads] over this wave's 9 k-steps of the tile at
+  // `tb`: four accumulation chains (token block x head block); one K read feeds
+  // both head blocks.
+  auto qk = [&](const DCP_LDS uint8_t* tb, f32x4 (&sacc)[2][2]) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) sacc[a][0] = sacc[a][1] = f32x4{};
+    bf16x8 r[kPrefetchK][2];
 #pragma unroll
     for (int s = 0; s < kPrefetchK; ++s)
-      r[s] = *(const DCP_LDS bf16x8*)(tb + kb[s & 1] + 128 * (s >> 1));
 #pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-      const bf16x8 a = r[s % kPrefetchK];
+      for (int t = 0; t < 2; ++t) r[s][t] = *(const DCP_LDS bf16x8*)(tb + kb[t] + 128 * s);
+#pragma unroll
+    for (int s = 0; s < kKStepsWave; ++s) {
+      bf16x8 a[2] = {r[s % kPrefetchK][0], r[s % kPrefetchK][1]};
       const int sn = s + kPrefetchK;
-      if (sn < kKSteps) r[s % kPrefetchK] = *(const DCP_LDS bf16x8*)(tb + kb[sn & 1] + 128 * (sn >> 1));
-      sacc[0][s & 1] = mfma16x16x32(a, qreg[0][s], sacc[0][s & 1]);
-      sacc[1][s & 1] = mfma16x16x32(a, qreg[1][s], sacc[1][s & 1]);
-    }
-    // Keep kPrefetchK operand reads in flight: reads first, then (2 MFMA, 1 read) ...
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetchK, 0);
+      if (sn < kKStepsWave) {
 #pragma unroll
-    for (int s = 0; s < kKSteps - kPrefetchK; ++s) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPrefetchK, 0);
-    o0 = (sacc[0][0] + sacc[0][1]) * p.scale_log2;
-    o1 = (sacc[1][0] + sacc[1][1]) * p.scale_log2;
-  };
-
-  // Running softmax state of the tile whose P.V is next: per head block, the
-  // maximum (log2 units), the sum, and P^T of the tile as the B operand.
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  bf16x8 pb[2];
-  float alpha[2];
-  bool moved = false;
-  // Softmax over the 32 scores per head (elements 0..3: first token half, rows
-  // 4 q4 + j; 4..7: second half).  Both waves of a head half evaluate it on the
-  // same values in the same order and so agree bit for bit.
-  auto softmax = [&](const f32x4 (&h0)[2], const f32x4 (&h1)[2]) {
-    moved = false;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float x[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { x[j] = h0[hb][j]; x[j + 4] = h1[hb][j]; }
-      float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      mloc = max_over_groups(mloc);
-      const float m_new = mloc > m_run[hb] + kRescaleSlack ? mloc : m_run[hb];
-      alpha[hb] = fast_exp2(m_run[hb] - m_new);
-      moved |= m_new != m_run[hb];
-      float lsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pr = fast_exp2(x[j] - m_new);
-        lsum += pr;
-        pb[hb][j] = (__bf16)pr;
+        for (int t = 0; t < 2; ++t) r[s % kPrefetchK][t] = *(const DCP_LDS bf16x8*)(tb + kb[t] + 128 * sn);
       }
-      lsum = sum_over_groups(lsum);
-      l_run[hb] = l_run[hb] * alpha[hb] + lsum;
-      m_run[hb] = m_new;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sacc[t][0] = mfma16x16x32(a[t], qreg[0][s], sacc[t][0]);
+        sacc[t][1] = mfma16x16x32(a[t], qreg[1][s], sacc[t][1]);
+      }
     }
+    // Keep kPrefetchK steps of operand reads in flight: reads first, then
+    // (4 MFMA, 2 reads) ...
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetchK, 0);
+#pragma unroll
+    for (int s = 0; s < kKStepsWave - kPrefetchK; ++s) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4 * kPrefetchK, 0);
   };
 
-  f32x4 oacc[2][kVBlocks];
+  // Running softmax state of this lane's head: maximum (log2 units), sum, and P^T
+  // of the tile as the B operand of its P.V.
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  bf16x8 pb;
+  float alpha = 1.f;
+  bool moved = false;
+  // Softmax over the tile's 32 scores of this lane's head (x[0..3]: tokens 4 q4 + j,
+  // x[4..7]: tokens 16 + 4 q4 + j).
+  auto softmax = [&](const f32x4& s0, const f32x4& s1) {
+    float x[8];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb)
+    for (int j = 0; j < 4; ++j) { x[j] = s0[j]; x[j + 4] = s1[j]; }
+    float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mloc = max_over_groups(mloc);
+    const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
+    alpha = fast_exp2(m_run - m_new);
+    moved = m_new != m_run;
+    float lsum = 0.f;
 #pragma unroll
-    for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] = f32x4{};
+    for (int j = 0; j < 8; ++j) {
+      const float pr = fast_exp2(x[j] - m_new);
+      lsum += pr;
+      pb[j] = (__bf16)pr;
+    }
+    lsum = sum_over_groups(lsum);
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+  };
 
-  // O^T [256 dims x 32 heads] += V^T [256 x 32 tokens] P^T [32 x 32] for the tile at
+  f32x4 oacc[kVBlocks];
+#pragma unroll
+  for (int m = 0; m < kVBlocks; ++m) oacc[m] = f32x4{};
+
+  // O^T [512 dims x 16 heads] += V^T [512 x 32 tokens] P^T [32 x 16] for the tile at
   // `tb`, with this wave's copies of a later tile (into `stage`) spread between the
   // MFMAs: the copy asm orders itself with the LDS reads around it, so its place in
   // the source is its place in the instruction stream.  Source lane l16 of each
@@ -370,8 +371,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
 #pragma unroll
       for (int k = 0; k < C::kCopies; ++k)
         if (k * kVBlocks / C::kCopies == m) issue_copy(k, stage);
-      oacc[0][m] = mfma16x16x32(a, pb[0], oacc[0][m]);
-      oacc[1][m] = mfma16x16x32(a, pb[1], oacc[1][m]);
+      oacc[m] = mfma16x16x32(a, pb, oacc[m]);
     }
   };
 
@@ -383,15 +383,10 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
       zero_lds16(lds_addr(tb + (nvalid + (e >> 6)) * kRowBytes + (e & 63) * 16));
   };
 
-  // Mask the scores of tokens past the end (rows 16 tt + 4 q4 + j of the tile).
-  auto mask_scores = [&](f32x4& o0, f32x4& o1, int nvalid) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (16 * tt + 4 * q4 + j >= nvalid) o0[j] = o1[j] = -INFINITY;
-  };
-
-  const uint32_t xch_own = lds_addr((const DCP_LDS f32x4*)s_xch + (hh * 4 + tt * 2) * 64 + lane);
-  const uint32_t xch_half = lds_addr((const DCP_LDS f32x4*)s_xch + hh * 4 * 64 + lane);
+  // Exchange slots: this wave writes the partial of the partner's head block, reads
+  // the partner's partial of its own.
+  const uint32_t xch_out = lds_addr((const DCP_LDS f32x4*)s_xch + (hh * 4 + kk * 2) * 64 + lane);
+  const uint32_t xch_in = lds_addr((const DCP_LDS f32x4*)s_xch + (hh * 4 + (kk ^ 1) * 2) * 64 + lane);
 
   // ---- prologue: query slice, then three tiles in flight
   load_q(cc.b);
@@ -428,9 +423,8 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     const int nvalid = cur.Lr - cur.t * kTile;  // >= kTile for every tile but a request's last
     if (nvalid < kTile) zero_tail(tb, nvalid);
 
-    f32x4 o0, o1;
-    qk(tb, o0, o1);
-    if (nvalid < kTile) mask_scores(o0, o1, nvalid);
+    f32x4 sacc[2][2];
+    qk(tb, sacc);
     // The next request's query slice as soon as this one's last scores are done,
     // ahead of the copies issued below.
     if (i + 1 < total) {
@@ -440,19 +434,25 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
         q_after = issued;
       }
     }
-    write_scores(xch_own, o0, o1);
+    write_scores(xch_out, kk ? sacc[0][0] : sacc[0][1], kk ? sacc[1][0] : sacc[1][1]);
     wait_lgkm();
     wg_barrier();
-    {
-      f32x4 h0[2], h1[2];
-      read_scores(xch_half, h0, h1);
-      softmax(h0, h1);
+    f32x4 s0, s1;
+    read_scores(xch_in, s0, s1);
+    s0 = ((kk ? sacc[0][1] : sacc[0][0]) + s0) * p.scale_log2;
+    s1 = ((kk ? sacc[1][1] : sacc[1][0]) + s1) * p.scale_log2;
+    if (nvalid < kTile) {
+      // tokens past the end: rows 4 q4 + j (block 0) and 16 + 4 q4 + j (block 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (4 * q4 + j >= nvalid) s0[j] = -INFINITY;
+        if (16 + 4 * q4 + j >= nvalid) s1[j] = -INFINITY;
+      }
     }
+    softmax(s0, s1);
     if (__any(moved)) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] *= alpha[hb];
+      for (int m = 0; m < kVBlocks; ++m) oacc[m] *= alpha;
     }
     pv(tb, issued % kStages);
     ++issued;
@@ -462,32 +462,24 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     if (last_of_req || i == total - 1) {
       const bool whole = piece_t0 == 0 && last_of_req;
       const int64_t slot = 2 * w + (first_piece ? 0 : 1);
+      if (head < H) {
+        const float inv = 1.0f / l_run;
+        float* orow = (whole ? p.out_o + ((int64_t)cur.b * H + head) * kDv
+                             : p.ws_o + (slot * H + head) * kDv) + 4 * q4;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int head = head0 + 16 * hb;
-        if (head < H) {
-          const float inv = 1.0f / l_run[hb];
-          float* orow = whole ? p.out_o + ((int64_t)cur.b * H + head) * kDv
-                              : p.ws_o + (slot * H + head) * kDv;
-          orow += 256 * tt + 4 * q4;
-#pragma unroll
-          for (int m = 0; m < kVBlocks; ++m) *(f32x4*)(orow + 16 * m) = oacc[hb][m] * inv;
-          if (tt == 0 && q4 == 0) {
-            const float lse = (m_run[hb] + fast_log2(l_run[hb])) * kLn2;
-            if (whole) p.out_lse[(int64_t)cur.b * H + head] = lse;
-            else p.ws_lse[slot * H + head] = lse;
-          }
+        for (int m = 0; m < kVBlocks; ++m) *(f32x4*)(orow + 16 * m) = oacc[m] * inv;
+        if (q4 == 0) {
+          const float lse = (m_run + fast_log2(l_run)) * kLn2;
+          if (whole) p.out_lse[(int64_t)cur.b * H + head] = lse;
+          else p.ws_lse[slot * H + head] = lse;
         }
       }
       piece_t0 = 0;
       first_piece = false;
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-        for (int m = 0; m < kVBlocks; ++m) oacc[hb][m] = f32x4{};
-        m_run[hb] = -INFINITY;
-        l_run[hb] = 0.f;
-      }
+      for (int m = 0; m < kVBlocks; ++m) oacc[m] = f32x4{};
+      m_run = -INFINITY;
+      l_run = 0.f;
     }
     advance_loader();
   }
