@@ -401,6 +401,28 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   int piece_t0 = cc.t;       // first tile of the current piece inside request cc.b
   bool first_piece = true;
 
+  // A finished piece is stored at the top of the next iteration, right after its
+  // barrier and before that iteration's copies.  Stored at once, its stores would be
+  // the youngest memory operations at the next tile wait, which could then only be
+  // met by draining every copy in flight; deferred, they sit between two copy
+  // rounds, and the wait completes them together with the older round.
+  bool pend = false;
+  float pend_inv = 0.f, pend_lse = 0.f;
+  float* pend_o = nullptr;
+  float* pend_l = nullptr;
+  auto flush_piece = [&]() {
+    if (pend) {
+      if (head < H) {
+#pragma unroll
+        for (int m = 0; m < kVBlocks; ++m) *(f32x4*)(pend_o + 16 * m) = oacc[m] * pend_inv;
+        if (q4 == 0) *pend_l = pend_lse;
+      }
+#pragma unroll
+      for (int m = 0; m < kVBlocks; ++m) oacc[m] = f32x4{};
+      pend = false;
+    }
+  };
+
   for (int i = 0; i < total; ++i) {
     // Tile i (and the newest query slice) have landed once only the copy rounds
     // issued after both are outstanding; younger memory operations only make the
@@ -418,6 +440,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     // The loader's scalar loads were issued an iteration ago; retiring them here
     // lets the operand reads below wait for single LDS accesses, not for lgkmcnt(0).
     wait_lgkm();
+    flush_piece();
     const DCP_LDS uint8_t* tb = lds + (i % kStages) * kTileBytes;
     const Cursor cur = cc;
     const int nvalid = cur.Lr - cur.t * kTile;  // >= kTile for every tile but a request's last
@@ -457,32 +480,26 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     pv(tb, issued % kStages);
     ++issued;
 
-    // ---- end of a request piece: normalise and store, then start the next request
+    // ---- end of a request piece: its normalisation and destination; the stores
+    // follow after the next barrier
     const bool last_of_req = cur.t == cur.ntile - 1;
     if (last_of_req || i == total - 1) {
       const bool whole = piece_t0 == 0 && last_of_req;
       const int64_t slot = 2 * w + (first_piece ? 0 : 1);
-      if (head < H) {
-        const float inv = 1.0f / l_run;
-        float* orow = (whole ? p.out_o + ((int64_t)cur.b * H + head) * kDv
-                             : p.ws_o + (slot * H + head) * kDv) + 4 * q4;
-#pragma unroll
-        for (int m = 0; m < kVBlocks; ++m) *(f32x4*)(orow + 16 * m) = oacc[m] * inv;
-        if (q4 == 0) {
-          const float lse = (m_run + fast_log2(l_run)) * kLn2;
-          if (whole) p.out_lse[(int64_t)cur.b * H + head] = lse;
-          else p.ws_lse[slot * H + head] = lse;
-        }
-      }
+      pend = true;
+      pend_inv = 1.0f / l_run;
+      pend_lse = (m_run + fast_log2(l_run)) * kLn2;
+      const int hd = head < H ? head : 0;
+      pend_o = (whole ? p.out_o + ((int64_t)cur.b * H + hd) * kDv : p.ws_o + (slot * H + hd) * kDv) + 4 * q4;
+      pend_l = whole ? p.out_lse + (int64_t)cur.b * H + hd : p.ws_lse + slot * H + hd;
       piece_t0 = 0;
       first_piece = false;
-#pragma unroll
-      for (int m = 0; m < kVBlocks; ++m) oacc[m] = f32x4{};
       m_run = -INFINITY;
       l_run = 0.f;
     }
     advance_loader();
   }
+  flush_piece();
   // No copy may still be landing in this work-group's LDS when it exits.
   wait_vmcnt_builtin<0>();
 }
