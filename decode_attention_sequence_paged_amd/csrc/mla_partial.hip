@@ -14,8 +14,7 @@
 //  * Tiles stream HBM -> LDS through a 4-stage ring of 16-byte direct-to-LDS copies
 //    (no VGPR staging).  A tile is 32 rows of 72 16-byte slots; inside each row the
 //    chunks are XOR-swizzled in groups of 8, which makes both operand read patterns
-//    (16 rows x one chunk for K, 8 rows x 32 bytes for the transposed V reads) free
-//    of LDS bank conflicts while a tile stays exactly 36 copy instructions.
+//    free of LDS bank conflicts while a tile stays exactly 36 copy instructions.
 //  * The work-group is a grid of waves: head halves (32 heads each) x partners.  The
 //    two partners of a head half split the 576 score dims (even / odd 32-dim
 //    steps): each computes partial scores of its 32 heads against all 32 tokens of
@@ -65,11 +64,14 @@ constexpr int kSchedDsRead = 0x100;
 
 // XOR swizzle of the chunks of tile row r inside their aligned group of 8.  With a
 // row stride of 72 slots (8 mod 16), the 16-byte bank group of (r, c) is
-// 8*(r%2) + (c ^ x(r)) mod 16; x(r) = 2*((r>>1)&3) + ((r>>3)&1) gives
-//  * 16 distinct groups for rows 16a..16a+15 at one chunk (K operand reads), and
-//  * 8 distinct group pairs for rows 8b..8b+7 at one even/odd chunk pair (the
-//    transposed V reads serve 32 lanes = 8 rows x 32 bytes per LDS pass).
-__device__ __forceinline__ constexpr int row_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
+// 8*(r%2) + (c ^ x(r)) mod 16.  gfx950 serves a ds_read_b128 in four passes of 16
+// lanes: within each half of the wave, the lane quads (lane / 4) of even popcount
+// form one pass and those of odd popcount the other (measured).  The K operand read
+// puts lane (q4, l16) on row l16 and chunk 4 s + q4 of one 32-dim step;
+// x(r) = r & 6 gives the 16 lanes of every pass 16 distinct bank groups, and it
+// keeps the transposed V read (64 lanes x 8 bytes: rows 4 q4 + l16/4, one even/odd
+// chunk pair) at two lanes per bank, which that read serves without conflict.
+__device__ __forceinline__ constexpr int row_swz(int r) { return r & 6; }
 
 // NH head halves of 32 heads per work-group; 2 * NH waves (head halves x partners).
 template <int NH>
