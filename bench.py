@@ -50,6 +50,17 @@ def parse():
     return ap.parse_args()
 
 
+def describe(wl) -> str:
+    if wl.kind == "mla":
+        kv = "576-dim latent KV (V = first 512)"
+    else:
+        kv = "%d KV heads of %d+%d dims" % (wl.num_kv_heads, wl.qk_dim, wl.v_dim)
+    return ("%s: %s decode, B=%d, %d query heads, %s, pages of %d tokens, N=%d ranks, "
+            "interleave I=%d, lengths median %d max %d; all N ranks' partials + N-way merge per step"
+            % (wl.name, wl.kind.upper(), wl.batch, wl.num_q_heads, kv, wl.block_size, wl.dcp_size,
+               wl.interleave, int(np.median(wl.lengths)), int(max(wl.lengths))))
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in ("mla_partial.hip", "dcp_device.h"):
@@ -58,15 +69,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_per_launch_alg: float):
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on this workload and on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload_name") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -100,7 +111,7 @@ def cpu_baseline(wl, budget_s: float):
         done.append(r)
         if t_math >= budget_s:
             break
-    kv_bytes = tokens * wl.qk_dim * 2
+    kv_bytes = tokens * (wl.qk_dim * 2 if wl.kind == "mla" else wl.num_kv_heads * (wl.qk_dim + wl.v_dim) * 2)
     return {
         "value": round(kv_bytes / t_math / 1e9, 4),
         "unit": "GB/s",
@@ -186,7 +197,9 @@ def main():
     t_merge = float(per_call[:, N].mean())
 
     H, Dqk, Dv = wl.num_q_heads, wl.qk_dim, wl.v_dim
-    row_bytes = Dqk * 2
+    # KV bytes per local token: MLA one 576-dim latent row serving as K and V; GQA a K
+    # and a V row per KV head.
+    row_bytes = Dqk * 2 if wl.kind == "mla" else wl.num_kv_heads * (Dqk + Dv) * 2
     local = np.array([rc.total_local for rc in ranks], dtype=np.float64)
     pages = np.array([int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum()) for rc in ranks])
     kv_bytes = local * row_bytes
@@ -199,7 +212,7 @@ def main():
     rank0_kv = float(kv_bytes[0] / (t_rank[0] * 1e-3) / 1e9)
     value = float(kv_bytes.sum() / (ms_per_step * 1e-3) / 1e9)
     step_event_ms = float(t_rank.sum() + t_merge)
-    traffic = measured_traffic(float(call_bytes.mean()))
+    traffic = measured_traffic(wl.name)
 
     out = {
         "metric": METRIC,
@@ -215,11 +228,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "%s: MLA decode, B=%d, %d query heads, 576-dim latent KV (V = first 512), "
-                        "pages of %d tokens, N=%d ranks, interleave I=%d, bimodal lengths "
-                        "(median %d, max %d), all N ranks' partials + N-way merge per step"
-                        % (wl.name, wl.batch, H, wl.block_size, N, wl.interleave,
-                           int(np.median(wl.lengths)), int(max(wl.lengths))),
+            "workload": describe(wl),
             "global_batch": wl.batch,
             "seq_len": int(np.median(wl.lengths)),
             "parallelism": "dcp%d emulated on 1 GPU" % N,
@@ -239,7 +248,7 @@ def main():
                                     / (MFMA_BF16_PEAK_TFLOPS * 1e12), 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "dcp_decode_partial (mla_partial_kernel + split_reduce_kernel), mean over ranks",
+            "kernel": "dcp_decode_partial (%s_partial_kernel + split_reduce_kernel), mean over ranks" % wl.kind,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
