@@ -199,4 +199,76 @@ __device__ __forceinline__ int32_t clamp_page(int32_t page, int64_t num_blocks) 
   return (page < 0 || (int64_t)page >= num_blocks) ? 0 : page;
 }
 
+
+constexpr int kTileTokens = 32;  // tokens per streamed tile (both kernels)
+
+// ------------------------------------------------------------------ tile cursor
+//
+// Position in a span's sequence of (request, tile) pairs, 32-bit and division free
+// inside the loops: the page of tile t is entry pk of the request's block-table row
+// and the tile starts at token kTileTokens * sub of that page (tpp tiles per page).
+struct Cursor {
+  int b, t, ntile, Lr, pk, sub;
+  const int32_t* bt_row;
+};
+
+__device__ __forceinline__ void cursor_request(Cursor& c, const PartialParams& p, int b) {
+  c.b = b;
+  c.Lr = (int)part_local_len(p.part, b);
+  c.ntile = (c.Lr + kTileTokens - 1) / kTileTokens;
+  c.bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
+}
+
+__device__ __forceinline__ void cursor_set(Cursor& c, const PartialParams& p, int tpp, int b, int t) {
+  cursor_request(c, p, b);
+  c.t = t;
+  c.pk = t / tpp;
+  c.sub = t - c.pk * tpp;
+}
+
+// Advance to the next tile; only called while the span has tiles left, so a
+// non-empty request follows whenever the current one is exhausted.
+__device__ __forceinline__ void cursor_next(Cursor& c, const PartialParams& p, int tpp) {
+  ++c.t;
+  if (++c.sub == tpp) { c.sub = 0; ++c.pk; }
+  if (c.t < c.ntile) return;
+  do cursor_request(c, p, c.b + 1); while (c.ntile == 0 && c.b + 1 < p.part.batch);
+  c.t = c.pk = c.sub = 0;
+}
+
+// Cross-lane reductions over the lanes l, l^16, l^32, l^48 (one head's four lane
+// groups) with the gfx950 row-swap permutes: applying the operation to the two
+// outputs of a swap of x with itself combines x with its partner lane.
+__device__ __forceinline__ float max_over_groups(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+  auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+  auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// s_waitcnt lgkmcnt(0) as a builtin, so the compiler's own wait counting knows every
+// earlier LDS access and scalar load has completed.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ uint32_t lds_addr(const DCP_LDS void* p) { return (uint32_t)(uintptr_t)p; }
+
+// ------------------------------------------------------------------ LDS and copy asm
+// 16-byte global -> LDS copy: lane i's bytes from base + off land at lds_dst + 16 i.
+// Also asm, for the same reason: the compiler then neither counts these copies nor
+// drains them before LDS accesses; the kernel's explicit vmcnt waits order them.
+// No memory clobber: the copies only write a stage that no access in flight
+// touches, so LDS reads may be scheduled freely around them.
+__device__ __forceinline__ void copy16(const uint8_t* base, uint32_t off, uint32_t lds_dst) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds_dst));
+}
+__device__ __forceinline__ void zero_lds16(uint32_t addr) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(u32x4{0u, 0u, 0u, 0u}) : "memory");
+}
+
 }  // namespace dcp

@@ -6,11 +6,27 @@
 // head h / G).  Output: normalised partial O [B,H,128] and LSE [B,H] over the
 // rank's tokens.
 //
-// Design for gfx950: one wave per KV head (up to 4 KV heads per work-group, so a
-// token's K row slice and V row slice of the group are contiguous 256*W bytes),
-// tiles of 32 tokens streamed HBM -> LDS by direct 16-byte loads into a two-stage
-// ring, v_mfma_f32_16x16x32_bf16 for S^T = K Q^T (16 heads on the columns) and for
-// O^T += V^T P^T (V^T through the transposing LDS read), online softmax in base 2.
+// Design for gfx950:
+//  * One wave per KV head, up to 4 KV heads per work-group, so a token's K slice and
+//    V slice of the group are contiguous (256 bytes per head).  The work-group owns a
+//    token-balanced span of the rank's 32-token tiles (same partitioning as the MLA
+//    kernel).
+//  * Tiles (K part + V part, 2 x 32 rows x 256 B per head) stream HBM -> LDS through
+//    a two-stage ring of 16-byte direct-to-LDS copies: the next tile is in flight
+//    while this one is computed.  A 32-token tile starts at a multiple of 32 and page
+//    boundaries fall at multiples of the block size (a multiple of 16), so each
+//    16-row half of a tile lies in one page: a copy's source is a per-tile scalar
+//    page base plus a precomputed 32-bit lane offset, with no per-token arithmetic.
+//  * Rows are XOR-swizzled inside each head's 16 chunks (x(r) = 2 (r & 7)): with the
+//    gfx950 pass grouping of ds_read_b128 (lane quads of even / odd popcount within
+//    each half-wave) the K operand reads hit 16 distinct bank groups per pass, and
+//    the transposing V read stays at two lanes per bank.
+//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the group's
+//    (up to 16) query heads on the columns, V^T through ds_read_b64_tr_b16; base-2
+//    online softmax with the same lazy rescale as the MLA kernel.
+//  * Rows of a request's partial last tile past its end are copied from the page
+//    (always inside the pool) and made inert: scores -inf, V part zeroed in LDS.
+//    Finished pieces are stored after the next barrier, ahead of the next copies.
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -19,34 +35,31 @@ namespace gqa {
 
 constexpr int kD = 128;
 constexpr int kHeadBytes = kD * 2;  // 256
-constexpr int kTile = 32;
+constexpr int kTile = kTileTokens;  // 32
 constexpr int kStages = 2;
+constexpr float kRescaleSlack = 8.0f;
+static_assert(kGqaTile == kTile, "tile size");
 
 template <int KVW>
 struct Cfg {
   static constexpr int kThreads = 64 * KVW;
-  static constexpr int kRowBytes = KVW * kHeadBytes;       // one token's slice of the group
-  static constexpr int kChunks = kRowBytes / 16;           // 16 * KVW
-  static constexpr int kHalfBytes = kTile * kRowBytes;     // K (or V) part of a stage
+  static constexpr int kRowBytes = KVW * kHeadBytes;        // one token's slice of the group
+  static constexpr int kChunks = kRowBytes / 16;            // 16 * KVW
+  static constexpr int kHalfBytes = kTile * kRowBytes;      // K (or V) part of a stage
   static constexpr int kStageBytes = 2 * kHalfBytes;
-  static constexpr int kLoads = kTile * kChunks / kThreads;  // 8 per thread for K, 8 for V
-  static constexpr int kLdsBytes = kStages * kStageBytes;
+  static constexpr int kCopies = kTile * kChunks / kThreads;  // 8 per wave for K, 8 for V
+  static constexpr int kRowsPerCopy = 64 / kChunks;         // rows one wave-wide copy covers
+  static_assert(kCopies == 8 && 16 % kRowsPerCopy == 0, "copy geometry");
 };
 
-// LDS byte offset of 16-byte chunk c of tile row `row`: chunks are rotated by the
-// row index (modulo the power-of-two chunk count) so that 16 rows read at the same
-// logical chunk hit different banks.
-template <int KVW>
-__device__ __forceinline__ int chunk_off(int row, int c) {
-  constexpr int CH = Cfg<KVW>::kChunks;
-  static_assert((CH & (CH - 1)) == 0, "chunk count must be a power of two");
-  return row * Cfg<KVW>::kRowBytes + ((c + row) & (CH - 1)) * 16;
-}
+// Chunk c (0 .. 16*KVW-1) of tile row r sits at position c ^ x(r) of the row; the
+// XOR stays inside the head's 16 chunks.
+__device__ __forceinline__ constexpr int row_swz(int r) { return 2 * (r & 7); }
 
 template <int KVW>
 __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams p) {
   using C = Cfg<KVW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::kStageBytes];
   __shared__ int64_t s_scan[C::kThreads];
   __shared__ int64_t s_loc[2];
 
@@ -60,172 +73,237 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   int hg;
   block_to_span(p.part.num_parts, p.num_head_groups, &w, &hg);
   const bool write_prefix = (w == 0 && hg == 0);
-  SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr, s_scan,
-                                         s_loc);
+  const SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
+                                               s_scan, s_loc);
   if (loc.start >= loc.end) return;
+  const int total = (int)(loc.end - loc.start);
+  const int bs = p.block_size;
+  const int tpp = bs >= kTile ? bs / kTile : 1;  // whole tiles per page (bs >= 32), else 1
 
   const int H = p.num_q_heads;
   const int Hkv = p.num_kv_heads;
   const int G = H / Hkv;
   const int g0 = hg * KVW;             // first KV head of the work-group
   const int g = g0 + wave;             // this wave's KV head
-  const int head = g * G + l16;        // this lane's query head (S^T column)
   const bool head_ok = l16 < G;
-
+  const int head = g * G + (head_ok ? l16 : 0);  // this lane's query head (S^T column)
+  const int64_t row_stride = (int64_t)Hkv * kHeadBytes;  // bytes between token rows in the pool
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
-  int ld_row[C::kLoads];
-  int ld_off[C::kLoads];
+  // This lane's copies: LDS slot s = (k * KVW + wave) * 64 + lane of a tile half is
+  // position s % kChunks of row s / kChunks, which holds chunk (pos ^ x(row)).  The
+  // source offset is relative to the row's 16-row half; copy k of this wave covers
+  // rows of one half only (hi_copy: the second).
+  uint32_t ld_off[C::kCopies];
+  bool hi_copy[C::kCopies];
 #pragma unroll
-  for (int k = 0; k < C::kLoads; ++k) {
+  for (int k = 0; k < C::kCopies; ++k) {
     const int s = (k * KVW + wave) * 64 + lane;
     const int row = s / C::kChunks;
-    const int pc = s - row * C::kChunks;
-    ld_row[k] = row;
-    ld_off[k] = ((pc - row) & (C::kChunks - 1)) * 16;   // inverse of chunk_off's rotation
+    const int pos = s - row * C::kChunks;
+    ld_off[k] = (uint32_t)((row & 15) * row_stride + g0 * kHeadBytes + (pos ^ row_swz(row)) * 16);
+    hi_copy[k] = ((k * KVW + wave) * C::kRowsPerCopy) >= 16;
   }
-  const int64_t row_stride = (int64_t)Hkv * kHeadBytes;  // bytes between token rows in the pool
 
-  int64_t remaining = loc.end - loc.start;
-  int b = loc.b0;
-  int64_t toff = loc.off0;
+  // Operand offsets inside a stage half.  K: token block mt, row 16 mt + l16, chunk
+  // 16 wave + 4 s + q4 -> ka[s] (+16 rows for mt = 1).  V: row 4 q4 + l16/4 (+16),
+  // dims 16 m + 4 (l16 % 4) .. +3 = chunk 16 wave + 2 m + (l16 % 4) / 2, byte half
+  // l16 % 2 -> va[m].
+  uint32_t ka[4], va[8];
+  {
+    const int r = l16;
+    const int x = row_swz(r);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      ka[s] = (uint32_t)(r * C::kRowBytes + wave * kHeadBytes + ((4 * s + q4) ^ x) * 16);
+  }
+  {
+    const int r = 4 * q4 + (l16 >> 2);
+    const int x = row_swz(r);
+    const int h = (l16 & 3) >> 1;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      va[m] = (uint32_t)(r * C::kRowBytes + wave * kHeadBytes + ((2 * m + h) ^ x) * 16 + 8 * (l16 & 1));
+  }
+
+  Cursor lc, cc;
+  cursor_set(lc, p, tpp, loc.b0, (int)loc.off0);
+  cc = lc;
+
+  // Copy source of the loader's tile: the pool byte offsets of its two 16-row halves.
+  // Past the end of the span the loader stays on the last tile, which is copied again
+  // into a stage no wave reads.
+  int lc_left = total;
+  int64_t src_lo = 0, src_hi = 0;
+  auto next_src = [&]() {
+    const int64_t tok0 = (int64_t)lc.t * kTile;
+    const int64_t t1 = tok0 + 16;
+    const int32_t pg0 = clamp_page(ld_const(lc.bt_row + tok0 / bs), p.num_cache_blocks);
+    // A second half with no valid row may lie past the request's last page (and past
+    // its block-table row): it then reuses the first half's page, in bounds.
+    const int32_t pg1 = lc.Lr - tok0 > 16 ? clamp_page(ld_const(lc.bt_row + t1 / bs), p.num_cache_blocks)
+                                          : pg0;
+    src_lo = ((int64_t)pg0 * bs + tok0 % bs) * row_stride;
+    src_hi = ((int64_t)pg1 * bs + t1 % bs) * row_stride;
+  };
+  auto advance_loader = [&]() {
+    if (--lc_left > 0) {
+      cursor_next(lc, p, tpp);
+      next_src();
+    }
+  };
+  auto issue = [&](int stage) {
+    DCP_LDS uint8_t* kdst = lds + stage * C::kStageBytes;
+    DCP_LDS uint8_t* vdst = kdst + C::kHalfBytes;
+#pragma unroll
+    for (int k = 0; k < C::kCopies; ++k) {
+      const int64_t base = hi_copy[k] ? src_hi : src_lo;
+      copy16(p.k_cache + base, ld_off[k], lds_addr(kdst + (k * KVW + wave) * 1024));
+      copy16(p.v_cache + base, ld_off[k], lds_addr(vdst + (k * KVW + wave) * 1024));
+    }
+  };
+
+  // q[b, head, 32 s + 8 q4 .. +7]: the B operand of S^T = K Q^T for k-step s.  Lanes
+  // of heads past the group load the group's first head: their columns are
+  // independent of the others and never stored.
+  bf16x8 qreg[4];
+  auto load_q = [&](int b) {
+    const uint16_t* qp = p.q + ((int64_t)b * H + head) * kD + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qreg[s] = *(const bf16x8*)(qp + 32 * s);
+  };
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) oacc[m] = f32x4{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // Finished pieces are stored after the next barrier, before that iteration's copies.
+  bool pend = false;
+  float pend_inv = 0.f, pend_lse = 0.f;
+  float* pend_o = nullptr;
+  float* pend_l = nullptr;
+  auto flush_piece = [&]() {
+    if (pend) {
+      if (head_ok) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) *(f32x4*)(pend_o + 16 * m) = oacc[m] * pend_inv;
+        if (q4 == 0) *pend_l = pend_lse;
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) oacc[m] = f32x4{};
+      pend = false;
+    }
+  };
+
+  // Zero the V rows nvalid..31 of the tile at `vb` (the V half of a stage).
+  auto zero_tail = [&](DCP_LDS uint8_t* vb, int nvalid) {
+    const int n = (kTile - nvalid) * C::kChunks;
+    for (int e = tid; e < n; e += C::kThreads)
+      zero_lds16(lds_addr(vb + nvalid * C::kRowBytes + e * 16));
+  };
+
+  // ---- prologue: query slice and the first tile
+  load_q(cc.b);
+  next_src();
+  issue(0);
+  advance_loader();
+  int piece_t0 = cc.t;
   bool first_piece = true;
 
-  while (remaining > 0) {
-    const int64_t Lr = part_local_len(p.part, b);
-    const int64_t ntile = (Lr + kTile - 1) / kTile;
-    if (ntile == 0) { ++b; continue; }
-    const int64_t n = (ntile - toff) < remaining ? (ntile - toff) : remaining;
-    const bool whole = (toff == 0 && n == ntile);
-    const int32_t* bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
-
-    // q[b, head, 32*s + 8*q4 .. +7]
-    bf16x8 qreg[4];
-    {
-      const uint16_t* qp = p.q + ((int64_t)b * H + (head_ok ? head : g * G)) * kD + 8 * q4;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 v = *(const bf16x8*)(qp + 32 * s);
-        if (!head_ok) v = bf16x8{};
-        qreg[s] = v;
-      }
-    }
-
-    auto issue_tile = [&](int64_t t_local, int stage) {
-      const int64_t tok0 = t_local * kTile;
-      const int nvalid = (int)((Lr - tok0) < kTile ? (Lr - tok0) : kTile);
-      const int32_t page_lo = clamp_page(ld_const(bt_row + tok0 / p.block_size), p.num_cache_blocks);
-      int32_t page_hi = page_lo;
-      if (nvalid > 16)
-        page_hi = clamp_page(ld_const(bt_row + (tok0 + 16) / p.block_size), p.num_cache_blocks);
-      DCP_LDS uint8_t* kdst = lds + stage * C::kStageBytes;
-      DCP_LDS uint8_t* vdst = kdst + C::kHalfBytes;
-#pragma unroll
-      for (int k = 0; k < C::kLoads; ++k) {
-        const int row = ld_row[k] < nvalid ? ld_row[k] : nvalid - 1;
-        const int64_t tok = tok0 + row;
-        const int32_t page = row < 16 ? page_lo : page_hi;
-        const int64_t off = ((int64_t)page * p.block_size + tok % p.block_size) * row_stride +
-                            (int64_t)g0 * kHeadBytes + ld_off[k];
-        dma16(p.k_cache + off, kdst + (k * KVW + wave) * 1024);
-        dma16(p.v_cache + off, vdst + (k * KVW + wave) * 1024);
-      }
-    };
-
-    f32x4 oacc[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) oacc[m] = f32x4{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    issue_tile(toff, 0);
-    for (int64_t i = 0; i < n; ++i) {
-      wait_vmcnt<0>();
-      wg_barrier();
-      if (i + 1 < n) issue_tile(toff + i + 1, (int)((i + 1) & 1));
-
-      const DCP_LDS uint8_t* kb = lds + (int)(i & 1) * C::kStageBytes;
-      const DCP_LDS uint8_t* vb = kb + C::kHalfBytes;
-      const int64_t tok0 = (toff + i) * kTile;
-      const int nvalid = (int)((Lr - tok0) < kTile ? (Lr - tok0) : kTile);
-
-      // S^T [32 tokens x 16 heads] as two 16x16 tiles
-      f32x4 sacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int c = wave * 16 + 4 * s + q4;
-          const bf16x8 a = *(const DCP_LDS bf16x8*)(kb + chunk_off<KVW>(16 * mt + l16, c));
-          sacc[mt] = mfma16x16x32(a, qreg[s], sacc[mt]);
-        }
-      }
-
-      // online softmax; lane holds head l16, tokens 16*mt + 4*q4 + r
-      float x[8];
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = 16 * (j >> 2) + 4 * q4 + (j & 3);
-        x[j] = tok < nvalid ? sacc[j >> 2][j & 3] * p.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, x[j]);
-      }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = fast_exp2(m_run - m_new);
-      float lsum = 0.f;
-      bf16x8 pb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pr = fast_exp2(x[j] - m_new);
-        lsum += pr;
-        pb[j] = (__bf16)pr;
-      }
-      lsum += shfl_xor_f(lsum, 16);
-      lsum += shfl_xor_f(lsum, 32);
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
-      }
-
-      // O^T [128 dims x 16 heads] += V^T [128 x 32 tokens] P^T [32 x 16]
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int d0 = 16 * m + 4 * (l16 & 3);      // source lane's 4 dims
-        const int c = wave * 16 + (d0 >> 3);
-        const int hb = (d0 & 4) * 2;
-        const int r1 = 4 * q4 + (l16 >> 2);
-        const u32x2 v1 = lds_read_tr16(vb + chunk_off<KVW>(r1, c) + hb);
-        const u32x2 v2 = lds_read_tr16(vb + chunk_off<KVW>(r1 + 16, c) + hb);
-        const bf16x8 a = join_tr16(v1, v2);
-        oacc[m] = mfma16x16x32(a, pb, oacc[m]);
-      }
-    }
+  for (int i = 0; i < total; ++i) {
+    // Tile i (issued last iteration) and any query load have landed: this wave has
+    // nothing else outstanding but piece stores, which only make the wait stricter.
+    // The barrier then also guarantees every wave has finished tile i-1, whose stage
+    // the copies below refill.
+    wait_vmcnt_builtin<0>();
     wg_barrier();
+    wait_lgkm();
+    flush_piece();
+    issue((i + 1) & 1);
 
-    // epilogue: oacc[m] lane reg r -> dim 16m + 4*q4 + r, head l16
-    if (head_ok) {
-      const float inv = 1.0f / l_run;
-      const float lse = (m_run + fast_log2(l_run)) * kLn2;
-      const int64_t slot = 2 * w + (first_piece ? 0 : 1);
-      float* orow = whole ? p.out_o + ((int64_t)b * H + head) * kD : p.ws_o + (slot * H + head) * kD;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        *(f32x4*)(orow + 16 * m + 4 * q4) = oacc[m] * inv;
-      if (q4 == 0) {
-        if (whole) p.out_lse[(int64_t)b * H + head] = lse;
-        else p.ws_lse[slot * H + head] = lse;
-      }
+    DCP_LDS uint8_t* kb = lds + (i & 1) * C::kStageBytes;
+    DCP_LDS uint8_t* vb = kb + C::kHalfBytes;
+    const Cursor cur = cc;
+    const int nvalid = cur.Lr - cur.t * kTile;  // >= kTile for every tile but a request's last
+    if (nvalid < kTile) {
+      zero_tail(vb, nvalid);
+      wait_lgkm();
+      wg_barrier();
     }
 
-    remaining -= n;
-    first_piece = false;
-    ++b;
-    toff = 0;
+    // ---- S^T [32 tokens x 16 heads] as two 16x16 tiles
+    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 a0 = *(const DCP_LDS bf16x8*)(kb + ka[s]);
+      const bf16x8 a1 = *(const DCP_LDS bf16x8*)(kb + ka[s] + 16 * C::kRowBytes);
+      sacc[0] = mfma16x16x32(a0, qreg[s], sacc[0]);
+      sacc[1] = mfma16x16x32(a1, qreg[s], sacc[1]);
+    }
+    if (i + 1 < total) {
+      cursor_next(cc, p, tpp);
+      if (cc.b != cur.b) load_q(cc.b);
+    }
+
+    // ---- online softmax (base 2); lane: head l16, tokens 16 (j / 4) + 4 q4 + j % 4
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int tok = 16 * (j >> 2) + 4 * q4 + (j & 3);
+      x[j] = tok < nvalid ? sacc[j >> 2][j & 3] * p.scale_log2 : -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mloc = max_over_groups(mloc);
+    const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    float lsum = 0.f;
+    bf16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pr = fast_exp2(x[j] - m_new);
+      lsum += pr;
+      pb[j] = (__bf16)pr;
+    }
+    lsum = sum_over_groups(lsum);
+    l_run = l_run * alpha + lsum;
+    if (__any(m_new != m_run)) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
+    }
+    m_run = m_new;
+
+    // ---- O^T [128 dims x 16 heads] += V^T [128 x 32 tokens] P^T [32 x 16]
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const u32x2 v1 = lds_read_tr16(vb + va[m]);
+      const u32x2 v2 = lds_read_tr16(vb + va[m] + 16 * C::kRowBytes);
+      oacc[m] = mfma16x16x32(join_tr16(v1, v2), pb, oacc[m]);
+    }
+
+    // ---- end of a request piece: normalisation and destination; stored after the
+    // next barrier
+    const bool last_of_req = cur.t == cur.ntile - 1;
+    if (last_of_req || i == total - 1) {
+      const bool whole = piece_t0 == 0 && last_of_req;
+      const int64_t slot = 2 * w + (first_piece ? 0 : 1);
+      pend = true;
+      pend_inv = 1.0f / l_run;
+      pend_lse = (m_run + fast_log2(l_run)) * kLn2;
+      pend_o = (whole ? p.out_o + ((int64_t)cur.b * H + head) * kD : p.ws_o + (slot * H + head) * kD) + 4 * q4;
+      pend_l = whole ? p.out_lse + (int64_t)cur.b * H + head : p.ws_lse + slot * H + head;
+      piece_t0 = 0;
+      first_piece = false;
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+    advance_loader();
   }
+  flush_piece();
+  // No copy may still be landing in this work-group's LDS when it exits.
+  wait_vmcnt_builtin<0>();
 }
 
 }  // namespace gqa

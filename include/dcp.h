@@ -166,7 +166,7 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *   A request with no local tokens gets O_r = 0 and LSE_r = -inf.
  * Supported: MLA with qk_dim 576, v_dim 512, 1 <= H <= 128, block_size a
  * multiple of 32; GQA with qk_dim = v_dim = 128, H / num_kv_heads <= 16,
- * block_size a multiple of 16 or 16 a multiple of block_size.
+ * block_size a multiple of 16.
  * Errors: INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP (nothing runs on error). */
 dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
                                 const void* v_cache, int64_t num_cache_blocks,
