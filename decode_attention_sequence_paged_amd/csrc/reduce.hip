@@ -13,35 +13,49 @@
 namespace dcp {
 
 // ------------------------------------------------------------------ split-K reduce
-// One block of 256 threads per (request, group of heads); each thread owns 4
-// consecutive floats of one head's v_dim outputs (DV/4 threads per head).  The
-// pieces' slots and LSEs are first staged in LDS by the whole block, then every
-// thread folds the pieces in with eight independent loads in flight; pieces are
-// taken 256 at a time with an online maximum, so any count works.
-template <int DV>
-__global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceParams p) {
-  constexpr int kTph = DV / 4;         // threads per head
-  constexpr int kHpb = 256 / kTph;     // heads per block
-  constexpr int kChunk = 256;          // pieces staged per round
-  constexpr int kUnroll = 8;
-  static_assert(256 % kTph == 0, "head rows must tile the block");
+// One block per (request, group of heads).  A head's v_dim outputs are spread over
+// DV/4 threads (4 consecutive floats each); with PL > 1, PL such thread sets ("piece
+// lanes") fold every PL-th piece of the request and are summed through LDS at the
+// end.  The pieces' slots and LSEs are first staged in LDS by the whole block, a
+// chunk of kThreads pieces at a time with a running maximum, so any piece count
+// works.  The host picks PL from the expected pieces per request (partitions /
+// batch): 1 for batches of many requests, up to 8 for a single very long request.
+template <int DV, int PL>
+struct SplitCfg {
+  static constexpr int kQuads = DV / 4;                      // threads per head and piece lane
+  static constexpr int kTph = kQuads * PL;                   // threads per head
+  static constexpr int kThreads = kTph < 256 ? 256 : kTph;
+  static constexpr int kHpb = kThreads / kTph;               // heads per block
+  static constexpr int kUnroll = 4;
+  static_assert(kThreads % kTph == 0 && kThreads <= 1024, "block shape");
+};
+
+template <int DV, int PL>
+__global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_kernel(SplitReduceParams p) {
+  using C = SplitCfg<DV, PL>;
+  constexpr int kChunk = C::kThreads;  // pieces staged per round
   __shared__ int64_t s_slot[kChunk];
-  __shared__ float s_lse[kChunk][kHpb];
+  __shared__ float s_lse[kChunk][C::kHpb];
+  __shared__ f32x4 s_acc[PL > 1 ? C::kThreads : 1];
+  __shared__ float s_w[PL > 1 ? C::kThreads : 1];
 
   const int b = blockIdx.x;
-  const int head0 = blockIdx.y * kHpb;
-  const int hd = (int)threadIdx.x / kTph;
+  const int head0 = blockIdx.y * C::kHpb;
+  const int hd = (int)threadIdx.x / C::kTph;
   const int head = head0 + hd;
-  const int t = threadIdx.x % kTph;
+  const int t = (int)threadIdx.x % C::kTph;
+  const int q = t % C::kQuads;
+  const int pl = t / C::kQuads;
   const int H = p.num_heads;
+  const bool head_ok = head < H;
 
   const int64_t F = p.ws_prefix[b];
   const int64_t n = p.ws_prefix[b + 1] - F;
-  float* orow = p.out_o + ((int64_t)b * H + head) * DV + 4 * t;
-  if (n == 0) {
-    if (head < H) {
+  float* orow = p.out_o + ((int64_t)b * H + head) * DV + 4 * q;
+  if (n == 0) {  // no local tokens: the merge's neutral element
+    if (head_ok && pl == 0) {
       *(f32x4*)orow = f32x4{};
-      if (t == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
+      if (q == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
     }
     return;
   }
@@ -55,57 +69,81 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(SplitReduceParams p) 
   f32x4 acc = f32x4{};
   for (int64_t base = w_lo; base <= w_hi; base += kChunk) {
     const int cnt = (int)((w_hi - base + 1) < kChunk ? (w_hi - base + 1) : kChunk);
-    __syncthreads();  // previous round's LDS reads are done
-    for (int i = threadIdx.x; i < cnt; i += 256) {
+    __syncthreads();  // the previous round's LDS reads are done
+    for (int i = threadIdx.x; i < cnt; i += C::kThreads) {
       const int64_t w = base + i;
       const int64_t s0 = span_start(w, TT, P);
-      const bool empty = s0 == span_start(w + 1, TT, P);
-      const int64_t slot = empty ? -1 : 2 * w + (s0 < F ? 1 : 0);
+      const bool empty = s0 == span_start(w + 1, TT, P);      // an empty span holds no piece
+      const int64_t slot = empty ? -1 : 2 * w + (s0 < F ? 1 : 0);  // the span's first or last piece
       s_slot[i] = slot;
 #pragma unroll
-      for (int h = 0; h < kHpb; ++h)
-        s_lse[i][h] = (slot >= 0 && head0 + h < H) ? p.ws_lse[slot * H + head0 + h] : -INFINITY;
+      for (int h = 0; h < C::kHpb; ++h)
+        s_lse[i][h] = (slot >= 0 && head0 + h < H) ? p.ws_lse[slot * H + head0 + h] * kLog2e : -INFINITY;
     }
     __syncthreads();
-    if (head >= H) continue;
     float cm = -INFINITY;
     for (int i = 0; i < cnt; ++i) cm = fmaxf(cm, s_lse[i][hd]);
     const float nm = fmaxf(mx, cm);
-    const float rescale = mx == -INFINITY ? 0.f : fast_exp2((mx - nm) * kLog2e);
+    const float rescale = mx == -INFINITY ? 0.f : fast_exp2(mx - nm);
     acc *= rescale;
     wsum *= rescale;
     mx = nm;
-    for (int i0 = 0; i0 < cnt; i0 += kUnroll) {
-      f32x4 v[kUnroll];
-      float wt[kUnroll];
+    if (head_ok) {
+      for (int i0 = pl; i0 < cnt; i0 += PL * C::kUnroll) {
+        f32x4 v[C::kUnroll];
+        float wt[C::kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int i = i0 + u;
-        const int64_t slot = i < cnt ? s_slot[i] : -1;
-        wt[u] = slot >= 0 ? fast_exp2((s_lse[i][hd] - mx) * kLog2e) : 0.f;
-        v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * t) : f32x4{};
-      }
+        for (int u = 0; u < C::kUnroll; ++u) {
+          const int i = i0 + u * PL;
+          const int64_t slot = i < cnt ? s_slot[i] : -1;
+          wt[u] = slot >= 0 ? fast_exp2(s_lse[i][hd] - mx) : 0.f;
+          v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * q) : f32x4{};
+        }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        wsum += wt[u];
-        acc += wt[u] * v[u];
+        for (int u = 0; u < C::kUnroll; ++u) {
+          wsum += wt[u];
+          acc += wt[u] * v[u];
+        }
       }
     }
   }
-  if (head >= H) return;
+  if constexpr (PL > 1) {  // every piece lane used the same maximum: plain sums
+    s_acc[threadIdx.x] = acc;
+    s_w[threadIdx.x] = wsum;
+    __syncthreads();
+    if (pl != 0) return;
+    const int base = hd * C::kTph + q;
+#pragma unroll
+    for (int j = 1; j < PL; ++j) {
+      acc += s_acc[base + j * C::kQuads];
+      wsum += s_w[base + j * C::kQuads];
+    }
+  }
+  if (!head_ok) return;
   *(f32x4*)orow = acc * (1.0f / wsum);
-  if (t == 0) p.out_lse[(int64_t)b * H + head] = mx + fast_log2(wsum) * kLn2;
+  if (q == 0) p.out_lse[(int64_t)b * H + head] = (mx + fast_log2(wsum)) * kLn2;
+}
+
+template <int DV, int PL>
+static hipError_t launch_split(const SplitReduceParams& p, hipStream_t stream) {
+  using C = SplitCfg<DV, PL>;
+  dim3 grid(p.batch, (p.num_heads + C::kHpb - 1) / C::kHpb);
+  hipLaunchKernelGGL((split_reduce_kernel<DV, PL>), grid, dim3(C::kThreads), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
-  const int hpb = 256 / (p.v_dim / 4);
-  dim3 grid(p.batch, (p.num_heads + hpb - 1) / hpb);
-  if (p.v_dim == 512)
-    hipLaunchKernelGGL(split_reduce_kernel<512>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(split_reduce_kernel<128>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  // Expected pieces per request: about partitions / batch + 1.
+  const int64_t per = (int64_t)p.num_parts / p.batch + 1;
+  if (p.v_dim == 512) {
+    if (per <= 4) return launch_split<512, 1>(p, stream);
+    if (per <= 16) return launch_split<512, 2>(p, stream);
+    return launch_split<512, 8>(p, stream);
+  }
+  if (per <= 4) return launch_split<128, 1>(p, stream);
+  if (per <= 16) return launch_split<128, 4>(p, stream);
+  return launch_split<128, 16>(p, stream);
 }
 
 // ------------------------------------------------------------------ N-way merge
