@@ -63,7 +63,7 @@ def describe(wl) -> str:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("mla_partial.hip", "dcp_device.h"):
+    for name in ("mla_partial.hip", "reduce.hip", "dcp_device.h"):
         with open(os.path.join(ROOT, "decode_attention_sequence_paged_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
