@@ -248,7 +248,7 @@ def main():
                                     / (MFMA_BF16_PEAK_TFLOPS * 1e12), 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "dcp_decode_partial (%s_partial_kernel + split_reduce_kernel), mean over ranks" % wl.kind,
+            "kernel": "dcp_decode_partial (%s partial kernel + split_reduce_kernel), mean over ranks" % wl.kind,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -440,6 +440,359 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   wait_vmcnt_builtin<0>();
 }
 
+
+// ------------------------------------------------------------------ 64-head groups
+// A work-group of 8 waves (two per SIMD) in two roles, one tile apart:
+//  * score waves 0..3: wave s owns head block s (16 heads) and all 576 score dims.
+//    It computes S^T of tile j+1 (16x16x32 MFMA, four accumulation chains: token
+//    block x k-step parity), runs the online softmax and leaves P^T (bf16, laid out
+//    as the MFMA B operand), the rescale factor of each head and, at the end of a
+//    piece, 1/l in LDS; it stores the piece's LSE itself.
+//  * P.V waves 4..7: wave v owns output dims 128 v .. 128 v + 127 of all 64 heads
+//    (32 O^T accumulators of 16 dims x 16 heads).  During tile j's interval it
+//    rescales, accumulates O^T += V^T P^T for tile j, stores finished pieces, and
+//    issues the copies of tile j+3 into the stage tile j-1 has just released.
+// Each role therefore keeps the matrix pipe busy while the other waits on a
+// latency-bound step (the softmax, the copies), and the two meet once per tile at a
+// single barrier.  V^T is read from LDS once per tile (each P.V wave reads only
+// its own dims) and K four times (once per head block).
+namespace wide {
+constexpr int kThreads = 512;
+constexpr int kRoleWaves = 4;                   // waves per role
+constexpr int kCopies = kCopyInstr / kRoleWaves;  // 9 copy instructions per P.V wave and tile
+constexpr int kDimBlocks = kDv / 16 / kRoleWaves;  // 8 O^T dim blocks per P.V wave
+constexpr int kHeadBlocks = 4;
+constexpr int kPfK = 4;                         // K operand steps in flight (2 reads each)
+constexpr int kPfV = 4;                         // V^T operand blocks in flight (2 reads each)
+static_assert(kCopyInstr % kRoleWaves == 0, "copies must split evenly over the P.V waves");
+}  // namespace wide
+
+__global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(PartialParams p) {
+  using namespace wide;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
+  __shared__ __attribute__((aligned(16))) bf16x8 s_p[2][kHeadBlocks][64];  // [tile parity][head block][lane]
+  __shared__ __attribute__((aligned(16))) float s_alpha[2][16][kHeadBlocks];  // [parity][head in block][block]
+  __shared__ __attribute__((aligned(16))) float s_inv[2][16][kHeadBlocks];
+  __shared__ int64_t s_loc[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int l16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  int64_t w;
+  int hg;
+  block_to_span(p.part.num_parts, p.num_head_groups, &w, &hg);
+  const bool write_prefix = (w == 0 && hg == 0);
+  // The span scan's scratch lives in the first stage, before any copy lands there.
+  const SpanLoc loc = locate_span<kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
+                                            (int64_t*)smem, s_loc);
+  if (loc.start >= loc.end) return;
+  const int total = (int)(loc.end - loc.start);
+  const int tpp = p.block_size / kTile;
+  const int64_t page_bytes = (int64_t)p.block_size * kRowBytes;
+  const int H = p.num_q_heads;
+  const int hbase = hg * 64;
+  DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
+
+  Cursor cur0;
+  cursor_set(cur0, p, tpp, loc.b0, (int)loc.off0);
+
+  // Where a piece ending at `cur` goes: the request's final row if the span holds
+  // the whole request, else the span's first or last workspace slot.
+  struct Piece {
+    int t0;
+    bool first;
+  };
+  auto piece_row = [&](const Piece& pc, const Cursor& cur, int head, bool& whole) -> int64_t {
+    whole = pc.t0 == 0 && cur.t == cur.ntile - 1;
+    const int64_t slot = 2 * w + (pc.first ? 0 : 1);
+    return whole ? (int64_t)cur.b * H + head : slot * H + head;
+  };
+
+  if (wave < kRoleWaves) {
+    // ================================================================ score waves
+    const int sb = wave;                       // head block
+    const int head = hbase + 16 * sb + l16;   // this lane's score column
+    const bool head_ok = head < H;
+
+    // K operand of token block tb, k-step s: row 16 tb + l16, chunk 4 s + q4
+    // -> kb[tb][s & 1] + 128 (s >> 1) under the row swizzle.
+    uint32_t kb[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int r = 16 * tb + l16;
+      const int x = row_swz(r);
+#pragma unroll
+      for (int par = 0; par < 2; ++par)
+        kb[tb][par] = (uint32_t)(r * kRowBytes + 64 * (par ^ (x >> 2)) + 16 * (q4 ^ (x & 3)));
+    }
+
+    // q[b, head, 32 s + 8 q4 .. +7] for the 18 k-steps: the B operand of S^T = K Q^T.
+    // Not tracked by the compiler's wait counting: the explicit vmcnt wait before the
+    // barrier that precedes its first use covers it.
+    bf16x8 qreg[kKSteps];
+    auto load_q = [&](int b) {
+      const uint16_t* qp = p.q + ((int64_t)b * H + (head_ok ? head : 0)) * kDqk + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s)
+        asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(qreg[s]) : "v"(qp), "n"(64 * s) : "memory");
+    };
+
+    auto qk = [&](const DCP_LDS uint8_t* tb, f32x4& s0, f32x4& s1) {
+      f32x4 acc[2][2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{};
+      bf16x8 r[kPfK][2];
+#pragma unroll
+      for (int s = 0; s < kPfK; ++s)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) r[s][t] = *(const DCP_LDS bf16x8*)(tb + kb[t][s & 1] + 128 * (s >> 1));
+#pragma unroll
+      for (int s = 0; s < kKSteps; ++s) {
+        const bf16x8 a0 = r[s % kPfK][0], a1 = r[s % kPfK][1];
+        const int sn = s + kPfK;
+        if (sn < kKSteps) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            r[s % kPfK][t] = *(const DCP_LDS bf16x8*)(tb + kb[t][sn & 1] + 128 * (sn >> 1));
+        }
+        acc[0][s & 1] = mfma16x16x32(a0, qreg[s], acc[0][s & 1]);
+        acc[1][s & 1] = mfma16x16x32(a1, qreg[s], acc[1][s & 1]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPfK, 0);
+#pragma unroll
+      for (int s = 0; s < kKSteps - kPfK; ++s) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2 * kPfK, 0);
+      s0 = acc[0][0] + acc[0][1];
+      s1 = acc[1][0] + acc[1][1];
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;
+    Cursor sc = cur0;
+    Piece pc{sc.t, true};
+    bool q_pending = true;
+    load_q(sc.b);
+    wait_vmcnt_builtin<0>();
+    q_pending = false;
+    wg_barrier();  // tile 0 has landed
+
+    for (int j = 0; j < total; ++j) {
+      const Cursor cur = sc;
+      const int par = j & 1;
+      const DCP_LDS uint8_t* tb = lds + (j % kStages) * kTileBytes;
+      f32x4 s0, s1;
+      qk(tb, s0, s1);
+      if (j + 1 < total) {
+        cursor_next(sc, p, tpp);
+        if (sc.b != cur.b) {
+          load_q(sc.b);
+          q_pending = true;
+        }
+      }
+      s0 *= p.scale_log2;
+      s1 *= p.scale_log2;
+      const int nvalid = cur.Lr - cur.t * kTile;
+      if (nvalid < kTile) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (4 * q4 + e >= nvalid) s0[e] = -INFINITY;
+          if (16 + 4 * q4 + e >= nvalid) s1[e] = -INFINITY;
+        }
+      }
+      // online softmax over the tile's 32 scores of this lane's head (lazy rescale)
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = s0[e]; x[e + 4] = s1[e]; }
+      float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mloc = max_over_groups(mloc);
+      const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      bf16x8 pb;
+      float lsum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pr = fast_exp2(x[e] - m_new);
+        lsum += pr;
+        pb[e] = (__bf16)pr;
+      }
+      lsum = sum_over_groups(lsum);
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+      s_p[par][sb][lane] = pb;
+      if (q4 == 0) s_alpha[par][l16][sb] = alpha;
+      if (cur.t == cur.ntile - 1 || j == total - 1) {
+        bool whole;
+        const int64_t row = piece_row(pc, cur, head_ok ? head : 0, whole);
+        if (q4 == 0) {
+          s_inv[par][l16][sb] = 1.0f / l_run;
+          if (head_ok) (whole ? p.out_lse : p.ws_lse)[row] = (m_run + fast_log2(l_run)) * kLn2;
+        }
+        pc.t0 = 0;
+        pc.first = false;
+        m_run = -INFINITY;
+        l_run = 0.f;
+      }
+      // Every iteration ends at the barrier that starts the P.V waves' interval for
+      // tile j (the P.V waves pass one barrier more: the one before this loop).
+      if (q_pending) {
+        wait_vmcnt_builtin<0>();
+        q_pending = false;
+      }
+      wait_lgkm();
+      wg_barrier();
+    }
+  } else {
+    // ================================================================ P.V waves
+    const int v = wave - kRoleWaves;  // dims 128 v .. 128 v + 127
+
+    // This lane's copies: LDS slot s = (k * 4 + v) * 64 + lane of a tile.
+    uint32_t ld_off[kCopies];
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) {
+      const int s = (k * kRoleWaves + v) * 64 + lane;
+      const int row = s / kChunks;
+      const int pos = s - row * kChunks;
+      ld_off[k] = (uint32_t)(row * kRowBytes + (pos ^ row_swz(row)) * 16);
+    }
+    // V^T operand of dim block mm (dims 128 v + 16 mm ..): rows 4 q4 + l16 / 4 (+16),
+    // chunk 2 (8 v + mm) + (l16 % 4) / 2, byte half l16 % 2.
+    uint32_t vb[4];
+    {
+      const int r = 4 * q4 + (l16 >> 2);
+      const int x = row_swz(r);
+      const int h = (l16 & 3) >> 1;
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        vb[m] = (uint32_t)(r * kRowBytes + 32 * (m ^ (x >> 1)) + 16 * (h ^ (x & 1)) + 8 * (l16 & 1) + 256 * v);
+    }
+    auto voff = [&](int mm) { return vb[mm & 3] + 128 * (mm >> 2); };
+
+    Cursor lc = cur0;
+    int lc_left = total;
+    const uint8_t* src = nullptr;
+    auto next_src = [&]() {
+      const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+      src = p.k_cache + page * page_bytes + lc.sub * kTileBytes;
+    };
+    auto issue_tile = [&](int stage) {
+#pragma unroll
+      for (int k = 0; k < kCopies; ++k)
+        copy16(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * kRoleWaves + v) * 1024));
+      if (--lc_left > 0) {
+        cursor_next(lc, p, tpp);
+        next_src();
+      }
+    };
+
+    f32x4 oacc[kDimBlocks][kHeadBlocks];
+#pragma unroll
+    for (int m = 0; m < kDimBlocks; ++m)
+#pragma unroll
+      for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[m][hb] = f32x4{};
+
+    Cursor pc_cur = cur0;
+    Piece pc{pc_cur.t, true};
+
+    // A finished piece is stored at the top of the next interval, before that
+    // interval's copies: the tile wait at its end then covers the stores too, whatever
+    // their number.
+    bool pend = false;
+    f32x4 pend_inv;
+    float* pend_dst = nullptr;  // row of head hbase + l16; head block hb is 16 rows further
+    auto flush_piece = [&]() {
+      if (!pend) return;
+#pragma unroll
+      for (int hb = 0; hb < kHeadBlocks; ++hb) {
+        if (hbase + 16 * hb + l16 < H) {
+#pragma unroll
+          for (int m = 0; m < kDimBlocks; ++m)
+            *(f32x4*)(pend_dst + (int64_t)16 * hb * kDv + 16 * m) = oacc[m][hb] * pend_inv[hb];
+        }
+#pragma unroll
+        for (int m = 0; m < kDimBlocks; ++m) oacc[m][hb] = f32x4{};
+      }
+      pend = false;
+    };
+
+    // prologue: tiles 0 and 1 in flight; tile 0 landed before the first barrier
+    next_src();
+    issue_tile(0);
+    issue_tile(1);
+    wait_vmcnt_builtin<kCopies>();
+    wg_barrier();
+
+    for (int i = -1; i < total; ++i) {
+      flush_piece();
+      issue_tile((i + 3) % kStages);  // past the span's end: the last tile again, unread
+      if (i >= 0) {
+        const Cursor cur = pc_cur;
+        const int par = i & 1;
+        const DCP_LDS uint8_t* tb = lds + (i % kStages) * kTileBytes;
+        const int nvalid = cur.Lr - cur.t * kTile;
+        if (nvalid < kTile) {
+          // zero this wave's V dims of the rows past the request's end
+          const int n = (kTile - nvalid) * 16;
+          for (int e = lane; e < n; e += 64)
+            zero_lds16(lds_addr(tb + (nvalid + (e >> 4)) * kRowBytes + (16 * v + (e & 15)) * 16));
+        }
+        const f32x4 alpha = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
+        bf16x8 pP[kHeadBlocks];
+#pragma unroll
+        for (int hb = 0; hb < kHeadBlocks; ++hb) pP[hb] = s_p[par][hb][lane];
+        const bool moved = alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f;
+        if (__any(moved)) {
+#pragma unroll
+          for (int m = 0; m < kDimBlocks; ++m)
+#pragma unroll
+            for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[m][hb] *= alpha[hb];
+        }
+        u32x2 v1[kPfV], v2[kPfV];
+#pragma unroll
+        for (int m = 0; m < kPfV; ++m) {
+          v1[m] = lds_read_tr16(tb + voff(m));
+          v2[m] = lds_read_tr16(tb + voff(m) + 16 * kRowBytes);
+        }
+#pragma unroll
+        for (int m = 0; m < kDimBlocks; ++m) {
+          const bf16x8 a = join_tr16(v1[m % kPfV], v2[m % kPfV]);
+          const int mn = m + kPfV;
+          if (mn < kDimBlocks) {
+            v1[m % kPfV] = lds_read_tr16(tb + voff(mn));
+            v2[m % kPfV] = lds_read_tr16(tb + voff(mn) + 16 * kRowBytes);
+          }
+#pragma unroll
+          for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[m][hb] = mfma16x16x32(a, pP[hb], oacc[m][hb]);
+        }
+        if (cur.t == cur.ntile - 1 || i == total - 1) {
+          // 1/l of every head leaves LDS now: the next tile of this parity overwrites it
+          pend_inv = *(const DCP_LDS f32x4*)&s_inv[par][l16][0];
+          bool whole;
+          const int64_t row = piece_row(pc, cur, hbase + l16, whole);
+          pend_dst = (whole ? p.out_o : p.ws_o) + row * kDv + 128 * v + 4 * q4;
+          pend = true;
+          pc.t0 = 0;
+          pc.first = false;
+        }
+        if (i + 1 < total) cursor_next(pc_cur, p, tpp);
+      }
+      if (i + 1 < total) {
+        // tile i+2 has landed once only the copies of tile i+3 are outstanding
+        wait_vmcnt_builtin<kCopies>();
+        wg_barrier();
+      }
+    }
+    flush_piece();
+    // No copy may still be landing in this work-group's LDS when it exits.
+    wait_vmcnt_builtin<0>();
+  }
+}
+
 }  // namespace mla
 
 int mla_heads_per_group(int num_q_heads) { return num_q_heads <= 32 ? 32 : 64; }
@@ -449,7 +802,7 @@ hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   if (mla_heads_per_group(p.num_q_heads) == 32)
     hipLaunchKernelGGL(mla::mla_partial_kernel<1>, dim3(grid), dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(mla::mla_partial_kernel<2>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(mla::mla_partial_wide_kernel, dim3(grid), dim3(mla::wide::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
