@@ -57,6 +57,16 @@ dcp_status_t check_desc(const dcp_attn_desc_t* d, int32_t* head_groups) {
   return DCP_ERROR_INVALID_VALUE;
 }
 
+// Tiles of work charged to each request a work-group touches (see the partition
+// helpers in dcp_device.h): the query slice it reads and the fp32 output row it
+// writes, in units of the tile bytes it streams.  MLA: a 64-head group moves 72 KiB
+// of q and 128 KiB of O against 36 KiB per tile (about 5.6; 5 measured), a 32-head
+// group half of that; GQA: 12 KiB against 16 KiB per KV head.
+int32_t request_weight(const dcp_attn_desc_t* d) {
+  if (d->kind == DCP_KV_MLA_LATENT) return dcp::mla_heads_per_group(d->num_q_heads) == 64 ? 5 : 3;
+  return 1;
+}
+
 int32_t default_parts(int32_t head_groups) {
   int cus = device_cu_count();
   if (cus <= 0) cus = 256;
@@ -72,7 +82,7 @@ struct WsLayout {
 WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   WsLayout l;
   l.prefix = 256;
-  l.lse = l.prefix + align256(sizeof(int64_t) * ((size_t)batch + 1));
+  l.lse = l.prefix + align256(sizeof(int64_t) * 2 * ((size_t)batch + 1));
   l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
   l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);
   return l;
@@ -230,6 +240,7 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   p.part.block_size = desc->block_size;
   p.part.tile = desc->kind == DCP_KV_MLA_LATENT ? dcp::kMlaTile : dcp::kGqaTile;
   p.part.num_parts = parts;
+  p.part.req_weight = request_weight(desc);
   p.out_o = out_o;
   p.out_lse = out_lse;
   p.ws_prefix = (int64_t*)(ws + wl.prefix);
@@ -249,6 +260,7 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   r.num_heads = desc->num_q_heads;
   r.v_dim = desc->v_dim;
   r.num_parts = parts;
+  r.req_weight = p.part.req_weight;
   r.out_o = out_o;
   r.out_lse = out_lse;
   return hip_status(dcp::launch_split_reduce(r, s));

@@ -96,11 +96,18 @@ __device__ __forceinline__ T ld_const(const T* ptr) {
 // ------------------------------------------------------------------ work partitions
 //
 // A rank's local tokens of the whole batch are cut into tiles of T tokens (a tile
-// never crosses a request), and the concatenated tile sequence into P equal spans:
-// span w covers tiles [floor(w*TT/P), floor((w+1)*TT/P)), TT being the total.  A
-// request whose tiles fall into several spans is computed piecewise; each piece
-// writes a partial (O, LSE) into a workspace slot and a second kernel merges them.
-// Span w owns slots 2w (its first request piece) and 2w+1 (its last).
+// never crosses a request), and the concatenated tile sequence into P spans of
+// equal work.  Besides its tiles, every request a work-group touches costs it the
+// query slice and the output row it writes (for 64 MLA heads, about five tiles of
+// memory traffic), so each request with local tokens is charged A extra tiles,
+// placed in front of its own: request b occupies the weighted range [WP_b,
+// WP_(b+1)) with WP_(b+1) = WP_b + A + n_b, and its tile k sits at WP_b + A + k.
+// Span w covers the weighted range [floor(w*WT/P), floor((w+1)*WT/P)), WT being the
+// weighted total, i.e. the tiles whose weighted positions fall into it; a span
+// boundary inside a request's charge moves to that request's first tile.  A request
+// whose tiles fall into several spans is computed piecewise; each piece writes a
+// partial (O, LSE) into a workspace slot and a second kernel merges them.  Span w
+// owns slots 2w (its first request piece) and 2w+1 (its last).
 
 // Local length of request b actually processed (clamped to what its block table row holds).
 __device__ __forceinline__ int64_t part_local_len(const PartitionArgs& a, int b) {
@@ -114,12 +121,15 @@ __device__ __forceinline__ int64_t part_tiles(const PartitionArgs& a, int b) {
   return (part_local_len(a, b) + a.tile - 1) / a.tile;
 }
 
-__device__ __forceinline__ int64_t span_start(int64_t w, int64_t TT, int64_t P) { return w * TT / P; }
+// Weighted start of span w.
+__device__ __forceinline__ int64_t span_start(int64_t w, int64_t WT, int64_t P) { return w * WT / P; }
 
-// The span that holds tile t (0 <= t < TT).
-__device__ __forceinline__ int64_t span_of(int64_t t, int64_t TT, int64_t P) {
-  return ((t + 1) * P - 1) / TT;
+// The span that holds weighted position x (0 <= x < WT).
+__device__ __forceinline__ int64_t span_of(int64_t x, int64_t WT, int64_t P) {
+  return ((x + 1) * P - 1) / WT;
 }
+
+constexpr int kCountBits = 17;  // packed scan value: tiles << kCountBits | requests with tiles
 
 struct SpanLoc {
   int64_t total;   // TT
@@ -131,19 +141,24 @@ struct SpanLoc {
 
 // Block-cooperative: every thread of the block gets the location of span w.  If
 // prefix_out is non-null, the block also writes each request's first tile index
-// (prefix_out[b]) and the total (prefix_out[B]).  s_scan must hold blockDim.x
-// int64 values; s_loc two int64 values.
+// (prefix_out[b], the total at prefix_out[B]) and weighted position (prefix_out[B +
+// 1 + b], the weighted total at prefix_out[2 B + 1]).  s_scan must hold blockDim.x
+// int64 values; s_loc four int64 values.
 template <int NT>
 __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
                                int64_t* s_scan, int64_t* s_loc) {
+  constexpr int64_t kCountMask = (int64_t(1) << kCountBits) - 1;
   const int tid = threadIdx.x;
   const int per = (a.batch + NT - 1) / NT;
   const int b_lo = tid * per;
   const int b_hi = min(a.batch, b_lo + per);
   int64_t sum = 0;
-  for (int b = b_lo; b < b_hi; ++b) sum += part_tiles(a, b);
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int64_t n = part_tiles(a, b);
+    sum += (n << kCountBits) | (n > 0 ? 1 : 0);
+  }
   s_scan[tid] = sum;
-  if (tid == 0) { s_loc[0] = -1; s_loc[1] = 0; }
+  if (tid == 0) { s_loc[0] = -1; s_loc[1] = 0; s_loc[2] = 0; s_loc[3] = 0; }
   __syncthreads();
   // Hillis-Steele inclusive scan over the per-thread sums.
   for (int d = 1; d < NT; d <<= 1) {
@@ -154,26 +169,38 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
   }
   const int64_t incl = s_scan[tid];
   const int64_t excl = incl - sum;
-  SpanLoc loc;
-  loc.total = s_scan[NT - 1];
-  loc.start = span_start(w, loc.total, a.num_parts);
-  loc.end = span_start(w + 1, loc.total, a.num_parts);
-  if (prefix_out) {
-    int64_t acc = excl;
-    for (int b = b_lo; b < b_hi; ++b) { prefix_out[b] = acc; acc += part_tiles(a, b); }
-    if (tid == NT - 1) prefix_out[a.batch] = loc.total;
-  }
-  if (loc.start < loc.end && excl <= loc.start && loc.start < incl) {
-    int64_t acc = excl;
-    for (int b = b_lo; b < b_hi; ++b) {
-      const int64_t n = part_tiles(a, b);
-      if (loc.start < acc + n) { s_loc[0] = b; s_loc[1] = loc.start - acc; break; }
-      acc += n;
+  const int64_t tot = s_scan[NT - 1];
+  const int64_t A = a.req_weight;
+  const int64_t TT = tot >> kCountBits;
+  const int64_t WT = TT + A * (tot & kCountMask);
+  const int64_t x0 = span_start(w, WT, a.num_parts);
+  const int64_t x1 = span_start(w + 1, WT, a.num_parts);
+  // Walk this thread's requests; the one whose weighted range holds x0 (x1) gives
+  // the span's first (end) tile.
+  int64_t F = excl >> kCountBits;
+  int64_t WP = F + A * (excl & kCountMask);
+  for (int b = b_lo; b < b_hi; ++b) {
+    const int64_t n = part_tiles(a, b);
+    if (prefix_out) { prefix_out[b] = F; prefix_out[a.batch + 1 + b] = WP; }
+    if (n > 0) {
+      const int64_t wend = WP + A + n;
+      if (x0 < x1 && WP <= x0 && x0 < wend) {
+        const int64_t off = x0 - WP - A > 0 ? x0 - WP - A : 0;
+        s_loc[0] = b; s_loc[1] = off; s_loc[2] = F + off;
+      }
+      if (WP <= x1 && x1 < wend) s_loc[3] = F + (x1 - WP - A > 0 ? x1 - WP - A : 0);
+      F += n;
+      WP = wend;
     }
   }
+  if (prefix_out && tid == NT - 1) { prefix_out[a.batch] = TT; prefix_out[2 * a.batch + 1] = WT; }
   __syncthreads();
+  SpanLoc loc;
+  loc.total = TT;
   loc.b0 = (int32_t)s_loc[0];
   loc.off0 = s_loc[1];
+  loc.start = x0 < x1 ? s_loc[2] : 0;
+  loc.end = x0 < x1 ? (x1 >= WT ? TT : s_loc[3]) : 0;
   __syncthreads();  // s_loc / s_scan may be reused after this
   return loc;
 }

@@ -13,6 +13,7 @@ struct PartitionArgs {
   int32_t max_blocks_per_seq, block_size;
   int32_t tile;             // tokens per tile
   int32_t num_parts;        // P
+  int32_t req_weight;       // tiles of work charged to each request with local tokens
 };
 
 struct PartialParams {
@@ -28,16 +29,17 @@ struct PartialParams {
   PartitionArgs part;
   float* out_o;             // [B, H, v_dim]
   float* out_lse;           // [B, H]
-  int64_t* ws_prefix;       // [B + 1]
+  int64_t* ws_prefix;       // [2 (B + 1)]: tile prefix, then weighted prefix
   float* ws_lse;            // [2P, H]
   float* ws_o;              // [2P, H, v_dim]
 };
 
 struct SplitReduceParams {
-  const int64_t* ws_prefix;  // [B + 1] first tile of each request, total at [B]
+  const int64_t* ws_prefix;  // [2 (B + 1)]: first tile of each request (total at [B]), then
+                             // its weighted position (weighted total at [2 B + 1])
   const float* ws_lse;       // [2P, H]
   const float* ws_o;         // [2P, H, v_dim]
-  int32_t batch, num_heads, v_dim, num_parts;
+  int32_t batch, num_heads, v_dim, num_parts, req_weight;
   float* out_o;              // [B, H, v_dim]
   float* out_lse;            // [B, H]
 };

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   using C = Cfg<KVW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::kStageBytes];
   __shared__ int64_t s_scan[C::kThreads];
-  __shared__ int64_t s_loc[2];
+  __shared__ int64_t s_loc[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

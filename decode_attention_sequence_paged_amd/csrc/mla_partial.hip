@@ -112,7 +112,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) f32x4 s_xch[NH * 2 * 2 * 64];  // [hh][writer kk][token block][lane]
   __shared__ int64_t s_scan[C::kThreads];
-  __shared__ int64_t s_loc[2];
+  __shared__ int64_t s_loc[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
   __shared__ __attribute__((aligned(16))) bf16x8 s_p[2][kHeadBlocks][64];  // [tile parity][head block][lane]
   __shared__ __attribute__((aligned(16))) float s_alpha[2][16][kHeadBlocks];  // [parity][head in block][block]
   __shared__ __attribute__((aligned(16))) float s_inv[2][16][kHeadBlocks];
-  __shared__ int64_t s_loc[2];
+  __shared__ int64_t s_loc[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

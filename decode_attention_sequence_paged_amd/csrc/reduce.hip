@@ -59,10 +59,13 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
     }
     return;
   }
-  const int64_t TT = p.ws_prefix[p.batch];
+  // weighted positions of the request's first and last tiles
+  const int64_t WP = p.ws_prefix[p.batch + 1 + b];
+  const int64_t WT = p.ws_prefix[2 * p.batch + 1];
+  const int64_t xF = WP + p.req_weight;
   const int64_t P = p.num_parts;
-  const int64_t w_lo = span_of(F, TT, P);
-  const int64_t w_hi = span_of(F + n - 1, TT, P);
+  const int64_t w_lo = span_of(xF, WT, P);
+  const int64_t w_hi = span_of(xF + n - 1, WT, P);
   if (w_lo == w_hi) return;  // computed in one piece by the partial kernel
 
   float mx = -INFINITY, wsum = 0.f;
@@ -72,9 +75,11 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
     __syncthreads();  // the previous round's LDS reads are done
     for (int i = threadIdx.x; i < cnt; i += C::kThreads) {
       const int64_t w = base + i;
-      const int64_t s0 = span_start(w, TT, P);
-      const bool empty = s0 == span_start(w + 1, TT, P);      // an empty span holds no piece
-      const int64_t slot = empty ? -1 : 2 * w + (s0 < F ? 1 : 0);  // the span's first or last piece
+      const int64_t x0 = span_start(w, WT, P);
+      const bool empty = x0 == span_start(w + 1, WT, P);  // an empty span holds no piece
+      // The first span may start before the request (it is that span's last piece);
+      // every later one starts inside it (its first piece).
+      const int64_t slot = empty ? -1 : 2 * w + (w == w_lo && x0 < WP ? 1 : 0);
       s_slot[i] = slot;
 #pragma unroll
       for (int h = 0; h < C::kHpb; ++h)
