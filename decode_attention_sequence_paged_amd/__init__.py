@@ -53,6 +53,8 @@ _SIGS = {
     "dcp_decode_partial": (_i32, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _i64, _vp, _i32, _vp,
                                   _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "dcp_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "dcp_append_kv": (_i32, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp,
+                             _i32, _i32, _i32, _i32, _vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -171,6 +173,16 @@ def dcp_decode_partial(desc: AttnDesc, q, k_cache, v_cache, block_table, seq_len
         _dptr(block_table), block_table.shape[1], _dptr(seq_lens), batch, rank, num_ranks,
         interleave, num_partitions, _dptr(workspace), workspace.numel() * workspace.element_size(),
         _dptr(out_o), _dptr(out_lse), _stream(stream)))
+
+
+def dcp_append_kv(desc: AttnDesc, new_k, new_v, k_cache, v_cache, block_table, seq_lens,
+                  rank: int, num_ranks: int, interleave: int, stream=None) -> None:
+    """Write each request's newest token row into the owning rank's page (see
+    include/dcp.h); a rank's call touches only the requests it owns."""
+    _check("dcp_append_kv", lib().dcp_append_kv(
+        ctypes.byref(desc), _dptr(new_k), _dptr(new_v), _dptr(k_cache), _dptr(v_cache),
+        k_cache.shape[0], _dptr(block_table), block_table.shape[1], _dptr(seq_lens),
+        new_k.shape[0], rank, num_ranks, interleave, _stream(stream)))
 
 
 def dcp_merge(o_parts, lse_parts, out_o, out_lse, stream=None) -> None:

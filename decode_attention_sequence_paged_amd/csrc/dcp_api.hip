@@ -266,6 +266,32 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   return hip_status(dcp::launch_split_reduce(r, s));
 }
 
+dcp_status_t dcp_append_kv(const dcp_attn_desc_t* desc, const void* new_k, const void* new_v,
+                           void* k_cache, void* v_cache, int64_t num_cache_blocks,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, int32_t rank,
+                           int32_t num_ranks, int32_t interleave, void* stream) {
+  int32_t groups = 0;
+  dcp_status_t st = check_desc(desc, &groups);
+  if (st != DCP_SUCCESS) return st;
+  st = check_shard_args(num_ranks, interleave, rank);
+  if (st != DCP_SUCCESS) return st;
+  if (batch < 0 || batch > kMaxBatch || max_blocks_per_seq < 1 || num_cache_blocks < 1)
+    return DCP_ERROR_INVALID_VALUE;
+  if (batch == 0) return DCP_SUCCESS;
+  const bool mla = desc->kind == DCP_KV_MLA_LATENT;
+  if (!new_k || !k_cache || !block_table || !seq_lens) return DCP_ERROR_INVALID_VALUE;
+  if (mla != (new_v == nullptr) || mla != (v_cache == nullptr)) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)new_k | (uintptr_t)new_v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return DCP_ERROR_INVALID_VALUE;
+  const int32_t row_k = desc->num_kv_heads * desc->qk_dim * 2;
+  const int32_t row_v = mla ? 0 : desc->num_kv_heads * desc->v_dim * 2;
+  return hip_status(dcp::launch_append(new_k, new_v, k_cache, v_cache, num_cache_blocks, block_table,
+                                       max_blocks_per_seq, seq_lens, batch, rank, num_ranks,
+                                       interleave, desc->block_size, row_k, row_v,
+                                       (hipStream_t)stream));
+}
+
 dcp_status_t dcp_merge(const float* o_parts, const float* lse_parts, int32_t num_parts,
                        int32_t batch, int32_t num_heads, int32_t v_dim, float* out_o,
                        float* out_lse, void* stream) {

@@ -16,6 +16,11 @@ int gqa_kv_heads_per_group(int num_kv_heads);
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream);
+hipError_t launch_append(const void* new_k, const void* new_v, void* k_cache, void* v_cache,
+                         int64_t num_cache_blocks, const int32_t* block_table,
+                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                         int32_t rank, int32_t num_ranks, int32_t interleave, int32_t block_size,
+                         int32_t row_k_bytes, int32_t row_v_bytes, hipStream_t stream);
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int32_t num_parts, int64_t rows,
                         int32_t v_dim, float* out_o, float* out_lse, hipStream_t stream);
 hipError_t launch_shard_map(const int32_t* seq_lens, int32_t batch, int32_t N, int32_t I,

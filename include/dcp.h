@@ -154,9 +154,11 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *                request's local length from (seq_lens, rank, num_ranks,
  *                interleave).
  *   num_partitions  work partitions per head group (0 = default).  The rank's
- *                local tokens are cut into this many equal token ranges across
- *                the batch; a request cut between partitions is reduced in a
- *                second kernel (split-K).
+ *                local tokens are cut into this many consecutive ranges of equal
+ *                work across the batch (tiles of 32 tokens, each request also
+ *                charged a few tiles for its query and output traffic); a
+ *                request cut between partitions is reduced in a second kernel
+ *                (split-K).
  *   workspace    device, >= dcp_decode_workspace_size(desc, batch, num_partitions)
  *                bytes, 256-byte aligned; contents need no initialisation.
  *   out_o        device fp32 [batch, H, v_dim], written: normalised partial output
@@ -175,6 +177,35 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
                                 int32_t num_ranks, int32_t interleave, int32_t num_partitions,
                                 void* workspace, size_t workspace_bytes, float* out_o,
                                 float* out_lse, void* stream);
+
+/* ------------------------------------------------------------------ KV append
+ * Blog Sec. 4 ("What is DCP?") and Sec. 2.2: every rank stores the KV of its own
+ * token positions only, so the KV row of a newly decoded token goes to the one
+ * rank that owns its position.  With seq_lens counting the new token, request b's
+ * new token sits at global position t = seq_lens[b] - 1; its owner is
+ * (t / I) % N, its local index j = (t / (N*I)) * I + t % I, and its row is
+ * written to slot j % block_size of page block_table[b][j / block_size].
+ *
+ * Each rank calls this on its own cache with the same arguments apart from
+ * `rank`, `block_table` and the caches; a call writes the rows of the requests the
+ * rank owns and nothing else.
+ *   new_k     device bf16 [batch, qk_dim] (MLA: the 576-dim latent row) or
+ *             [batch, num_kv_heads, qk_dim] (GQA)
+ *   new_v     GQA: device bf16 [batch, num_kv_heads, v_dim]; MLA: NULL
+ *   k_cache, v_cache  the rank's page pools, laid out as for dcp_decode_partial
+ *             (v_cache NULL for MLA); num_cache_blocks pages.
+ *   block_table  device int32 [batch, max_blocks_per_seq], the rank's pages.
+ *   seq_lens  device int32 [batch]: global lengths including the new token.
+ * A request with seq_lens[b] <= 0, a local index past max_blocks_per_seq pages,
+ * or a page id outside [0, num_cache_blocks) gets no write (nothing else is
+ * touched).  The rows written must not be read by work running concurrently.
+ * Supported: the shapes dcp_decode_partial supports.
+ * Errors: INVALID_VALUE, NOT_SUPPORTED, HIP (nothing runs on error).          */
+dcp_status_t dcp_append_kv(const dcp_attn_desc_t* desc, const void* new_k, const void* new_v,
+                           void* k_cache, void* v_cache, int64_t num_cache_blocks,
+                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, int32_t rank,
+                           int32_t num_ranks, int32_t interleave, void* stream);
 
 /* ------------------------------------------------------------------ merge
  * Blog Sec. 4.1, "AllGather + ReduceScatter": the LSE values reweight and merge

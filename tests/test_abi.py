@@ -79,8 +79,8 @@ def test_host_argument_errors():
 def test_workspace_size_and_desc_validation():
     mla = dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 128, 576 ** -0.5)
     n = dcp.dcp_decode_workspace_size(mla, 128, 256)
-    # prefix [B+1] int64, 2P x H LSE, 2P x H x 512 O (each 256-byte aligned) + header
-    assert n >= 256 + 8 * 129 + 4 * 2 * 256 * 64 * 513
+    # prefixes 2 (B+1) int64, 2P x H LSE, 2P x H x 512 O (each 256-byte aligned) + header
+    assert n >= 256 + 8 * 2 * 129 + 4 * 2 * 256 * 64 * 513
     assert dcp.dcp_decode_workspace_size(mla, 128, 0) > 0
     bad = [
         dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 2, 576, 512, 128, 0.1),   # MLA has one KV head
@@ -123,3 +123,29 @@ def test_partial_rejects_bad_arguments_before_launching():
     assert lib.dcp_merge(fake, fake, 0, 2, 2, 512, fake, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
     assert lib.dcp_merge(fake, fake, 2, 2, 2, 510, fake, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
     assert lib.dcp_merge(fake, fake, 2, 0, 2, 512, fake, fake, 0) == dcp.DCP_SUCCESS
+
+
+def test_append_rejects_bad_arguments_before_launching():
+    import ctypes
+    lib = dcp.lib()
+    mla = dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 128, 0.05)
+    gqa = dcp.attn_desc(dcp.DCP_KV_GQA, 64, 4, 128, 128, 16, 0.05)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    def call(desc=mla, nk=fake, nv=0, k=fake, v=0, nb=10, bt=fake, mb=4, sl=fake, B=2, rank=0, N=2, I=1):
+        return lib.dcp_append_kv(ctypes.byref(desc), nk, nv, k, v, nb, bt, mb, sl, B, rank, N, I, 0)
+    assert call(rank=2) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(rank=-1) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(N=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(I=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(nv=fake) == dcp.DCP_ERROR_INVALID_VALUE        # MLA has no separate V row
+    assert call(v=fake) == dcp.DCP_ERROR_INVALID_VALUE         # ... nor a V cache
+    assert call(nk=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(k=fake + 8) == dcp.DCP_ERROR_INVALID_VALUE     # misaligned
+    assert call(nb=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(mb=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(B=-1) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(B=0) == dcp.DCP_SUCCESS                         # empty batch: nothing to do
+    assert call(desc=gqa) == dcp.DCP_ERROR_INVALID_VALUE        # GQA needs V row and cache
+    assert call(desc=gqa, nv=fake) == dcp.DCP_ERROR_INVALID_VALUE
+    bad = dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 48, 0.05)
+    assert call(desc=bad) == dcp.DCP_ERROR_NOT_SUPPORTED

@@ -335,3 +335,109 @@ def test_full_size_mla(name):
             pr = [oracle_rank(wl, b, r) for r in range(wl.dcp_size)]
             Of, Lf = oracle.merge([p[0] for p in pr], [p[1] for p in pr])
         check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Of, Lf, "%s merged b%d" % (name, b))
+
+
+def _new_rows(wl, tokens):
+    """Device bf16 rows of the tokens at global positions tokens[b] (one per request),
+    from the seeded generator: MLA [B, 576]; GQA K [B, Hkv, 128] and V [B, Hkv, 128]."""
+    B = len(tokens)
+    t = torch.tensor([(b << di.ROW_T_BITS) + int(tokens[b]) for b in range(B)], dtype=torch.int64,
+                     device="cuda")
+    if wl.kind == "mla":
+        nk = torch.empty((B, wl.qk_dim), dtype=torch.bfloat16, device="cuda")
+        di.device_fill_rows(nk.view(torch.int16), torch.arange(B, device="cuda"), t, wl.qk_dim,
+                            wl.seed, di.STREAM_K)
+        return nk, None
+    H = wl.num_kv_heads
+    g = torch.arange(H, dtype=torch.int64, device="cuda")
+    ids = (t[:, None] * H + g[None, :]).reshape(-1)
+    dst = torch.arange(B * H, dtype=torch.int64, device="cuda")
+    nk = torch.empty((B, H, wl.qk_dim), dtype=torch.bfloat16, device="cuda")
+    nv = torch.empty((B, H, wl.v_dim), dtype=torch.bfloat16, device="cuda")
+    di.device_fill_rows(nk.view(torch.int16), dst, ids, wl.qk_dim, wl.seed, di.STREAM_K)
+    di.device_fill_rows(nv.view(torch.int16), dst, ids, wl.v_dim, wl.seed, di.STREAM_V)
+    return nk, nv
+
+
+@pytest.mark.parametrize("kind,N,I,bs,steps", [("mla", 8, 128, 128, 5), ("mla", 3, 5, 32, 40),
+                                               ("gqa", 4, 1, 16, 9), ("gqa", 2, 3, 32, 20)])
+def test_kv_append_fills_owner_slots(kind, N, I, bs, steps):
+    """Decode steps that append one token per request on every rank: afterwards each
+    rank's pools are bit-identical to pools built directly for the longer lengths
+    (rows are indexed by logical (request, position), so both hold the same values at
+    the same slots).  Owner rank and local index come from the oracle's enumeration;
+    appended slots start poisoned, and no other slot may change."""
+    pg = _paged()
+    L0 = np.array([1000, 0, 1, 3 * N * I + 7, 2 * bs - 1], dtype=np.int64)
+    L1 = L0 + steps
+    name = "mla_tiny" if kind == "mla" else "gqa_b32"
+    wl = _wl(name, batch=len(L0), lengths=L1, dcp_size=N, interleave=I, block_size=bs)
+    desc = pg.desc_for(wl)
+    caches, refs = [], []
+    for r in range(N):
+        rc = pg.build_rank_cache(wl, r, lengths=L1)
+        refs.append((rc.k_cache.clone(), None if rc.v_cache is None else rc.v_cache.clone()))
+        bt = rc.block_table.cpu().numpy()
+        rows = []
+        for b in range(len(L0)):
+            toks = oracle.rank_tokens(int(L1[b]), N, I, r)
+            for j, t in enumerate(toks):
+                if t >= L0[b]:
+                    rows.append(int(bt[b, j // bs]) * bs + j % bs)
+        if rows:
+            idx = torch.tensor(rows, dtype=torch.int64, device="cuda")
+            for pool in (rc.k_cache, rc.v_cache):
+                if pool is not None:
+                    pool.view(pool.shape[0] * bs, -1).view(torch.int16)[idx] = di.BF16_NAN_BITS
+        caches.append(rc)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        seq = torch.tensor((L0 + s + 1).astype(np.int32), device="cuda")
+        nk, nv = _new_rows(wl, L0 + s)
+        for r in range(N):
+            rc = caches[r]
+            dcp.dcp_append_kv(desc, nk, nv, rc.k_cache, rc.v_cache, rc.block_table, seq, r, N, I)
+    torch.cuda.synchronize()
+    for r in range(N):
+        rk, rv = refs[r]
+        assert torch.equal(caches[r].k_cache.view(torch.int16), rk.view(torch.int16)), "rank %d K" % r
+        if rv is not None:
+            assert torch.equal(caches[r].v_cache.view(torch.int16), rv.view(torch.int16)), "rank %d V" % r
+
+
+def test_kv_append_then_attention_matches_oracle():
+    """The appended cache serves the next decode step: partial attention of every rank
+    over the appended pools, merged, equals the oracle's full attention at the new
+    lengths."""
+    pg = _paged()
+    N, I, bs, steps = 2, 1, 64, 3
+    L0 = np.array([1000, 3000], dtype=np.int64)
+    L1 = L0 + steps
+    wl = _wl("mla_tiny", lengths=L1, dcp_size=N, interleave=I, block_size=bs)
+    desc = pg.desc_for(wl)
+    q = pg.device_query(wl)
+    o_all = torch.empty((N, wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+    l_all = torch.empty((N, wl.batch, wl.num_q_heads), device="cuda")
+    for r in range(N):
+        rc = pg.build_rank_cache(wl, r, lengths=L1)
+        bt = rc.block_table.cpu().numpy()
+        rows = [int(bt[b, j // bs]) * bs + j % bs for b in range(wl.batch)
+                for j, t in enumerate(oracle.rank_tokens(int(L1[b]), N, I, r)) if t >= L0[b]]
+        if rows:
+            rc.k_cache.view(-1, wl.qk_dim).view(torch.int16)[torch.tensor(rows, device="cuda")] = \
+                di.BF16_NAN_BITS
+        for s in range(steps):
+            seq = torch.tensor((L0 + s + 1).astype(np.int32), device="cuda")
+            nk, _ = _new_rows(wl, L0 + s)
+            dcp.dcp_append_kv(desc, nk, None, rc.k_cache, None, rc.block_table, seq, r, N, I)
+        sl = torch.tensor(L1.astype(np.int32), device="cuda")
+        ws = pg.workspace_for(wl)
+        pg.run_partial(wl, rc, q, sl, o_all[r], l_all[r], ws)
+    o = torch.empty_like(o_all[0])
+    lse = torch.empty_like(l_all[0])
+    dcp.dcp_merge(o_all, l_all, o, lse)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        o_ref, l_ref = oracle.full_attention(wl, b)
+        check_close(o[b].cpu().numpy()[None], lse[b].cpu().numpy()[None], o_ref[None], l_ref[None],
+                    "append+attention b=%d" % b)
