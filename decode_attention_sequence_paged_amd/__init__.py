@@ -23,6 +23,13 @@ DCP_ERROR_HIP = 4
 
 DCP_KV_MLA_LATENT = 0
 DCP_KV_GQA = 1
+DCP_DTYPE_F32 = 0
+DCP_DTYPE_BF16 = 1
+
+
+def _torch():
+    import torch
+    return torch
 
 
 class DcpError(RuntimeError):
@@ -55,6 +62,9 @@ _SIGS = {
     "dcp_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "dcp_append_kv": (_i32, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp,
                              _i32, _i32, _i32, _i32, _vp]),
+    "dcp_merge_lse": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "dcp_rescale_partial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "dcp_sum_head_slice": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -183,6 +193,30 @@ def dcp_append_kv(desc: AttnDesc, new_k, new_v, k_cache, v_cache, block_table, s
         ctypes.byref(desc), _dptr(new_k), _dptr(new_v), _dptr(k_cache), _dptr(v_cache),
         k_cache.shape[0], _dptr(block_table), block_table.shape[1], _dptr(seq_lens),
         new_k.shape[0], rank, num_ranks, interleave, _stream(stream)))
+
+
+def dcp_merge_lse(lse_parts, out_lse, stream=None) -> None:
+    """Global LSE [B,H] from the gathered per-rank LSEs [N,B,H]."""
+    N, B, H = lse_parts.shape
+    _check("dcp_merge_lse", lib().dcp_merge_lse(_dptr(lse_parts), N, B, H, _dptr(out_lse),
+                                                _stream(stream)))
+
+
+def dcp_rescale_partial(o_r, lse_r, lse, out, stream=None) -> None:
+    """out = exp(lse_r - lse) * o_r; out is float32 or bfloat16 [B,H,Dv]."""
+    B, H, Dv = o_r.shape
+    dt = DCP_DTYPE_BF16 if out.dtype == _torch().bfloat16 else DCP_DTYPE_F32
+    _check("dcp_rescale_partial", lib().dcp_rescale_partial(
+        _dptr(o_r), _dptr(lse_r), _dptr(lse), B, H, Dv, dt, _dptr(out), _stream(stream)))
+
+
+def dcp_sum_head_slice(scaled_parts, rank: int, out, stream=None) -> None:
+    """Rank `rank`'s head slice of the sum over the stacked scaled partials
+    [N,B,H,Dv] (float32 or bfloat16); out float32 [B, H/N, Dv]."""
+    N, B, H, Dv = scaled_parts.shape
+    dt = DCP_DTYPE_BF16 if scaled_parts.dtype == _torch().bfloat16 else DCP_DTYPE_F32
+    _check("dcp_sum_head_slice", lib().dcp_sum_head_slice(
+        _dptr(scaled_parts), dt, N, B, H, Dv, rank, _dptr(out), _stream(stream)))
 
 
 def dcp_merge(o_parts, lse_parts, out_o, out_lse, stream=None) -> None:

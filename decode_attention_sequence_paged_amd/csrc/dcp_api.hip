@@ -304,4 +304,41 @@ dcp_status_t dcp_merge(const float* o_parts, const float* lse_parts, int32_t num
                                       (hipStream_t)stream));
 }
 
+dcp_status_t dcp_merge_lse(const float* lse_parts, int32_t num_parts, int32_t batch,
+                           int32_t num_heads, float* out_lse, void* stream) {
+  if (num_parts < 1 || batch < 0 || num_heads < 0) return DCP_ERROR_INVALID_VALUE;
+  const int64_t rows = (int64_t)batch * num_heads;
+  if (rows == 0) return DCP_SUCCESS;
+  if (!lse_parts || !out_lse) return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_merge_lse(lse_parts, num_parts, rows, out_lse, (hipStream_t)stream));
+}
+
+dcp_status_t dcp_rescale_partial(const float* o_r, const float* lse_r, const float* lse,
+                                 int32_t batch, int32_t num_heads, int32_t v_dim,
+                                 int32_t out_dtype, void* out, void* stream) {
+  if (batch < 0 || num_heads < 0 || v_dim < 4 || v_dim % 4) return DCP_ERROR_INVALID_VALUE;
+  if (out_dtype != DCP_DTYPE_F32 && out_dtype != DCP_DTYPE_BF16) return DCP_ERROR_INVALID_VALUE;
+  const int64_t rows = (int64_t)batch * num_heads;
+  if (rows == 0) return DCP_SUCCESS;
+  if (!o_r || !lse_r || !lse || !out) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)o_r & 15) || ((uintptr_t)out & (out_dtype == DCP_DTYPE_F32 ? 15 : 7)))
+    return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_rescale(o_r, lse_r, lse, rows, v_dim, out_dtype == DCP_DTYPE_BF16, out,
+                                        (hipStream_t)stream));
+}
+
+dcp_status_t dcp_sum_head_slice(const void* scaled_parts, int32_t in_dtype, int32_t num_parts,
+                                int32_t batch, int32_t num_heads, int32_t v_dim, int32_t rank,
+                                float* out, void* stream) {
+  if (num_parts < 1 || batch < 0 || num_heads < 0 || v_dim < 4 || v_dim % 4) return DCP_ERROR_INVALID_VALUE;
+  if (num_heads % num_parts || rank < 0 || rank >= num_parts) return DCP_ERROR_INVALID_VALUE;
+  if (in_dtype != DCP_DTYPE_F32 && in_dtype != DCP_DTYPE_BF16) return DCP_ERROR_INVALID_VALUE;
+  if ((int64_t)batch * num_heads == 0) return DCP_SUCCESS;
+  if (!scaled_parts || !out) return DCP_ERROR_INVALID_VALUE;
+  if (((uintptr_t)scaled_parts & (in_dtype == DCP_DTYPE_F32 ? 15 : 7)) || ((uintptr_t)out & 15))
+    return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_sum_slice(scaled_parts, in_dtype == DCP_DTYPE_BF16, num_parts, batch,
+                                          num_heads, rank, v_dim, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -16,6 +16,11 @@ int gqa_kv_heads_per_group(int num_kv_heads);
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream);
 hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream);
+hipError_t launch_merge_lse(const float* lse_parts, int32_t n, int64_t rows, float* out, hipStream_t s);
+hipError_t launch_rescale(const float* o, const float* lse_r, const float* lse, int64_t rows,
+                          int32_t v_dim, bool bf16, void* out, hipStream_t s);
+hipError_t launch_sum_slice(const void* parts, bool bf16, int32_t n, int64_t batch, int32_t heads,
+                            int32_t rank, int32_t v_dim, float* out, hipStream_t s);
 hipError_t launch_append(const void* new_k, const void* new_v, void* k_cache, void* v_cache,
                          int64_t num_cache_blocks, const int32_t* block_table,
                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,

@@ -223,6 +223,41 @@ dcp_status_t dcp_merge(const float* o_parts, const float* lse_parts, int32_t num
                        int32_t batch, int32_t num_heads, int32_t v_dim, float* out_o,
                        float* out_lse, void* stream);
 
+/* The same merge as the per-rank steps of a multi-GPU group (blog Sec. 4.1,
+ * "AllGather + ReduceScatter"): (1) after an all-gather of the LSE_r every rank
+ * computes the global LSE; (2) each rank scales its own partial by its share
+ * exp(LSE_r - LSE); (3) a reduce-scatter sums the scaled partials over the ranks,
+ * rank r keeping heads [r*H/N, (r+1)*H/N).  Concatenating the N slices of step 3
+ * gives dcp_merge's O; step 1 gives its LSE.  The scaled partials can travel as
+ * bf16, halving the reduce-scatter's bytes; each term then carries one bf16
+ * rounding (relative 2^-9) before the fp32 sum.                              */
+typedef enum { DCP_DTYPE_F32 = 0, DCP_DTYPE_BF16 = 1 } dcp_dtype_t;
+
+/* Step 1.  lse_parts device fp32 [num_parts, batch, H] (the gathered LSE_r);
+ * out_lse device fp32 [batch, H], written (-inf where every LSE_r is -inf).
+ * Errors: INVALID_VALUE for num_parts < 1, negative sizes or NULL pointers.  */
+dcp_status_t dcp_merge_lse(const float* lse_parts, int32_t num_parts, int32_t batch,
+                           int32_t num_heads, float* out_lse, void* stream);
+
+/* Step 2.  o_r device fp32 [batch, H, v_dim], lse_r and lse device fp32
+ * [batch, H]; out device [batch, H, v_dim] of out_dtype (dcp_dtype_t), written
+ * with exp(lse_r - lse) * o_r (0 where lse_r or lse is -inf).
+ * Errors: INVALID_VALUE for v_dim not a multiple of 4, a bad dtype, NULL or
+ * misaligned pointers.                                                        */
+dcp_status_t dcp_rescale_partial(const float* o_r, const float* lse_r, const float* lse,
+                                 int32_t batch, int32_t num_heads, int32_t v_dim,
+                                 int32_t out_dtype, void* out, void* stream);
+
+/* Step 3 for one rank.  scaled_parts device [num_parts, batch, H, v_dim] of
+ * in_dtype (the N ranks' step-2 outputs, stacked); out device fp32
+ * [batch, H / num_parts, v_dim], written with the sum over the parts of heads
+ * [rank * H/num_parts, (rank+1) * H/num_parts).
+ * Errors: INVALID_VALUE for H % num_parts != 0, rank outside [0, num_parts),
+ * v_dim not a multiple of 4, a bad dtype, NULL or misaligned pointers.       */
+dcp_status_t dcp_sum_head_slice(const void* scaled_parts, int32_t in_dtype, int32_t num_parts,
+                                int32_t batch, int32_t num_heads, int32_t v_dim, int32_t rank,
+                                float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

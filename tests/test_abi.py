@@ -149,3 +149,22 @@ def test_append_rejects_bad_arguments_before_launching():
     assert call(desc=gqa, nv=fake) == dcp.DCP_ERROR_INVALID_VALUE
     bad = dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 48, 0.05)
     assert call(desc=bad) == dcp.DCP_ERROR_NOT_SUPPORTED
+
+
+def test_merge_steps_reject_bad_arguments_before_launching():
+    lib = dcp.lib()
+    fake = 1 << 20
+    F32, BF16 = dcp.DCP_DTYPE_F32, dcp.DCP_DTYPE_BF16
+    assert lib.dcp_merge_lse(fake, 0, 2, 4, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_merge_lse(0, 2, 2, 4, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_merge_lse(fake, 2, 0, 4, fake, 0) == dcp.DCP_SUCCESS
+    assert lib.dcp_rescale_partial(fake, fake, fake, 2, 4, 510, F32, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_rescale_partial(fake, fake, fake, 2, 4, 512, 7, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_rescale_partial(fake, fake, fake, 2, 4, 512, F32, fake + 8, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_rescale_partial(fake, 0, fake, 2, 4, 512, BF16, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_rescale_partial(fake, fake, fake, 0, 4, 512, BF16, fake, 0) == dcp.DCP_SUCCESS
+    assert lib.dcp_sum_head_slice(fake, F32, 3, 2, 64, 512, 0, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE  # 64 % 3
+    assert lib.dcp_sum_head_slice(fake, F32, 4, 2, 64, 512, 4, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE  # rank
+    assert lib.dcp_sum_head_slice(fake, 5, 4, 2, 64, 512, 0, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_sum_head_slice(fake + 4, BF16, 4, 2, 64, 512, 0, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert lib.dcp_sum_head_slice(fake, BF16, 4, 0, 64, 512, 0, fake, 0) == dcp.DCP_SUCCESS

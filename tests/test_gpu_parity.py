@@ -441,3 +441,52 @@ def test_kv_append_then_attention_matches_oracle():
         o_ref, l_ref = oracle.full_attention(wl, b)
         check_close(o[b].cpu().numpy()[None], lse[b].cpu().numpy()[None], o_ref[None], l_ref[None],
                     "append+attention b=%d" % b)
+
+
+@pytest.mark.parametrize("name,kw", [("mla_tiny", {}),
+                                     ("mla_tiny", dict(dcp_size=4, interleave=64, lengths=(100, 5000))),
+                                     ("gqa_b32", dict(batch=6))])
+def test_merge_decomposition_equals_fused_merge(name, kw):
+    """The merge as per-rank steps (LSE all-gather -> global LSE; local rescale by
+    exp(LSE_r - LSE); reduce-scatter of the sums by head slice) equals dcp_merge, and
+    with fp32 or bf16 transport of the rescaled partials matches the oracle."""
+    wl = _wl(name, **kw)
+    if name == "gqa_b32":
+        wl = _wl(name, batch=6, lengths=tuple(int(x) for x in wl.lengths[:6]))
+    N, B, H, Dv = wl.dcp_size, wl.batch, wl.num_q_heads, wl.v_dim
+    pg = _paged()
+    q = pg.device_query(wl)
+    o_all = torch.empty((N, B, H, Dv), device="cuda")
+    l_all = torch.empty((N, B, H), device="cuda")
+    for r in range(N):
+        o, l, _ = run_rank(wl, r, q=q)
+        o_all[r] = o
+        l_all[r] = l
+    o_fused = torch.empty((B, H, Dv), device="cuda")
+    l_fused = torch.empty((B, H), device="cuda")
+    dcp.dcp_merge(o_all, l_all, o_fused, l_fused)
+    lse = torch.empty((B, H), device="cuda")
+    dcp.dcp_merge_lse(l_all, lse)
+    outs = {}
+    for dtype in (torch.float32, torch.bfloat16):
+        scaled = torch.empty((N, B, H, Dv), dtype=dtype, device="cuda")
+        for r in range(N):
+            dcp.dcp_rescale_partial(o_all[r], l_all[r], lse, scaled[r])
+        slices = []
+        for r in range(N):
+            sl = torch.empty((B, H // N, Dv), device="cuda")
+            dcp.dcp_sum_head_slice(scaled, r, sl)
+            slices.append(sl)
+        outs[dtype] = torch.cat(slices, dim=1)
+    torch.cuda.synchronize()
+    # the decomposition against the fused kernel (fp32 transport: rounding order only)
+    lf, ld = l_fused.cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lf), np.isneginf(ld))
+    fin = ~np.isneginf(lf)
+    assert np.abs(lf[fin] - ld[fin]).max() <= 1e-5
+    assert (outs[torch.float32] - o_fused).abs().max().item() <= 1e-5
+    for b in range(B):
+        o_ref, l_ref = oracle.full_attention(wl, b)
+        for dtype, o in outs.items():
+            check_close(o[b].cpu().numpy()[None], ld[b][None], o_ref[None], l_ref[None],
+                        "decomposed merge (%s) b=%d" % (dtype, b))
