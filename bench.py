@@ -12,6 +12,11 @@ Printed as one JSON line:
   rank0_kv_gbps    local-shard KV GB/s of rank 0's partial call (HIP events)
   roofline         the partial-attention call against the 8 TB/s HBM peak
   cpu_baseline     the float64 oracle on the host cores, per-rank partials of the batch
+
+With --bands it instead prints one JSON line with rank 0's partial-call bandwidth for
+each request-length band of the pages' comparison by sequence length (<32k, 32-64k,
+64-128k, 128-200k, >=200k tokens): the long-context MLA shape with requests drawn from
+the synthetic mix restricted to the band, as many as give rank 0 about 1.25M tokens.
 """
 from __future__ import annotations
 
@@ -44,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle math to time for the CPU baseline")
+    ap.add_argument("--bands", action="store_true",
+                    help="rank-0 partial bandwidth per request-length band instead of the step")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many bytes "
                          "(a reference for scaling the HBM byte counters of a profiler run)")
@@ -125,6 +132,62 @@ def cpu_baseline(wl, budget_s: float):
     }
 
 
+def run_bands(args):
+    """Rank 0's dcp_decode_partial call per length band (HIP events around each call)."""
+    import torch
+    import dcp_inputs as di
+    import decode_attention_sequence_paged_amd as dcp
+    from dcp_inputs import paged
+
+    dcp.lib()
+    torch.cuda.set_device(0)
+    rows = []
+    for lo, hi in di.LENGTH_BANDS:
+        wl = di.band_workload(lo, hi)
+        q = paged.device_query(wl)
+        sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+        rc = paged.build_rank_cache(wl, 0)
+        ws = paged.workspace_for(wl)
+        o = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+        lse = torch.empty((wl.batch, wl.num_q_heads), device="cuda")
+        for _ in range(args.warmup):
+            paged.run_partial(wl, rc, q, sl, o, lse, ws)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record()
+            paged.run_partial(wl, rc, q, sl, o, lse, ws)
+            b.record()
+        torch.cuda.synchronize()
+        t = float(np.mean([a.elapsed_time(b) for a, b in evs]))  # ms
+        H = wl.num_q_heads
+        pages = int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum())
+        kv = rc.total_local * wl.qk_dim * 2
+        call = kv + wl.batch * H * (wl.qk_dim * 2 + wl.v_dim * 4 + 4) + pages * 4
+        L = np.asarray(wl.lengths)
+        rows.append({
+            "band": "%d-%s" % (lo, "inf" if hi > di.MAX_SEQ_LEN else str(hi)),
+            "batch": wl.batch, "median_len": int(np.median(L)), "max_len": int(L.max()),
+            "rank0_local_tokens": int(rc.total_local), "call_ms": round(t, 4),
+            "rank0_kv_gbps": round(kv / (t * 1e-3) / 1e9, 1),
+            "roofline_frac": round(call / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "local_tokens_per_s": round(rc.total_local / (t * 1e-3), 1),
+        })
+        del q, sl, rc, ws, o, lse
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "rank-0 local-shard decode-attn KV GB/s by request length band",
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "MLA decode, 64 query heads, 576-dim latent KV (V = first 512), "
+                               "pages of 128 tokens, N=8 ranks, interleave I=128; rank 0's partial "
+                               "call; per band the synthetic length mix restricted to the band, "
+                               "batch sized for ~1.25M rank-0 tokens"},
+        "bands": rows,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -132,6 +195,10 @@ def main():
               "another on a single device, so --gpus %d is not supported." % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+
+    if args.bands:
+        run_bands(args)
+        return
 
     import torch
     import dcp_inputs as di

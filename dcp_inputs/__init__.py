@@ -239,6 +239,46 @@ def bimodal_lengths(batch: int, seed: int) -> np.ndarray:
     return np.array([bimodal_length_quantile(float(x)) for x in u], dtype=np.int64)
 
 
+def _band_u(length: int) -> float:
+    """Smallest u (to 1e-12) with bimodal_length_quantile(u) >= length."""
+    lo, hi = 0.0, 1.0
+    if bimodal_length_quantile(0.0) >= length:
+        return 0.0
+    for _ in range(60):
+        mid = 0.5 * (lo + hi)
+        if bimodal_length_quantile(mid) >= length:
+            hi = mid
+        else:
+            lo = mid
+    return hi
+
+
+def band_lengths(lo: int, hi: int, batch: int, seed: int) -> np.ndarray:
+    """``batch`` lengths of the synthetic mix restricted to [lo, hi): stratified
+    inverse-CDF draws over the part of the distribution that falls into the band,
+    shuffled with ``seed``."""
+    u0, u1 = _band_u(lo), _band_u(hi) if hi <= MAX_SEQ_LEN else 1.0
+    u = u0 + (np.arange(batch) + 0.5) / batch * (u1 - u0)
+    rng = np.random.default_rng([seed, STREAM_LENGTHS, lo])
+    u = u[rng.permutation(batch)]
+    L = np.array([bimodal_length_quantile(float(x)) for x in u], dtype=np.int64)
+    return np.clip(L, lo, min(hi, MAX_SEQ_LEN + 1) - 1)
+
+
+# The length bands of the pages' comparison by sequence length (blog Sec. 2.3).
+LENGTH_BANDS = ((0, 32768), (32768, 65536), (65536, 131072), (131072, 204800), (204800, MAX_SEQ_LEN + 1))
+
+
+def band_workload(lo: int, hi: int, local_tokens: int = 1_250_000, seed: int = 3) -> "Workload":
+    """The long-context MLA shape (64 heads, pages of 128, N = 8, I = 128) with requests
+    from one length band, as many as give rank 0 about ``local_tokens`` tokens."""
+    probe = band_lengths(lo, hi, 64, seed)
+    batch = int(min(4096, max(1, round(local_tokens * 8 / float(probe.mean())))))
+    L = band_lengths(lo, hi, batch, seed)
+    name = "mla_band_%dk_%s" % (lo // 1024, "inf" if hi > MAX_SEQ_LEN else "%dk" % (hi // 1024))
+    return Workload(name, "mla", batch, 64, 1, 576, 512, 128, 8, 128, seed, tuple(int(x) for x in L))
+
+
 def uniform_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng([seed, STREAM_LENGTHS])
     return rng.integers(lo, hi + 1, size=batch).astype(np.int64)

@@ -69,3 +69,19 @@ def test_workload_shapes():
     assert g.size == 32 and g.min() >= 4096 and g.max() <= 32768
     assert w["mla_1m"].lengths == (1048576,)
     assert len(w["mla_long_b128"].lengths) == 128 and len(w["mla_c512"].lengths) == 512
+
+
+def test_band_lengths_stay_in_band():
+    """Band draws come from the synthetic mix restricted to the band: every length is
+    inside it, and the draws follow the mix's quantiles there (a band that the mix covers
+    uniformly gets a near-uniform spread)."""
+    import dcp_inputs as di
+    for lo, hi in di.LENGTH_BANDS:
+        L = di.band_lengths(lo, hi, 200, seed=3)
+        assert L.min() >= max(lo, 1024) and L.max() < min(hi, di.MAX_SEQ_LEN + 1)
+    # 32k..64k lies inside the mix's uniform segment [8192, 65536): stratified draws are
+    # evenly spaced there
+    L = np.sort(di.band_lengths(32768, 65536, 64, seed=3))
+    assert abs(np.median(L) - 49152) < 600 and np.all(np.diff(L) > 0)
+    w = di.band_workload(65536, 131072)
+    assert abs(sum(w.lengths) / 8 - 1.25e6) < 0.02e6
