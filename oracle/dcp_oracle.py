@@ -30,6 +30,11 @@ Readings taken where the pages are silent (each is listed in the design notes):
   K is the whole latent row and V its first ``v_dim`` entries;
 * GQA query head ``h`` reads KV head ``h // (H / Hkv)``;
 * a single decode query attends every cached token (no mask);
+* multi-token decode queries (speculative decoding / multi-token prediction, blog
+  Sec. 6): the ``q_len`` queries are the request's last ``q_len`` positions, whose
+  K/V are already in the cache (``seq_lens`` counts them); query ``i`` attends the
+  positions ``<= L - q_len + i`` (causal by global position), so the last query sees
+  every token and ``q_len = 1`` is the single-token decode;
 * an empty token set gives ``O = 0`` and ``LSE = -inf``, the merge's neutral element.
 """
 from __future__ import annotations
@@ -155,3 +160,56 @@ def full_attention(wl, b: int, seed=None):
     L = int(wl.lengths[b])
     q, K, V = request_inputs(wl, b, np.arange(L, dtype=np.int64), seed)
     return attention(q, K, V, wl.softmax_scale)
+
+
+# ----------------------------------------------------------------------------- multi-token queries
+
+def causal_limits(L: int, q_len: int) -> np.ndarray:
+    """Last global position each of the ``q_len`` queries of a length-``L`` request sees."""
+    return L - q_len + np.arange(q_len, dtype=np.int64)
+
+
+def causal_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions, limits, scale: float):
+    """Multi-token decode attention in float64: query ``i`` attends the rows whose global
+    position is at most ``limits[i]``.
+
+    q: [Q, H, Dqk]; K: [T, Hkv, Dqk]; V: [T, Hkv, Dv]; positions: [T]; limits: [Q].
+    Returns (O [Q, H, Dv], LSE [Q, H]); a query that sees no row gets O = 0, LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    Q, H = q.shape[0], q.shape[1]
+    Dv = np.asarray(V).shape[2]
+    O = np.zeros((Q, H, Dv), dtype=np.float64)
+    LSE = np.full((Q, H), NEG_INF, dtype=np.float64)
+    for i in range(Q):
+        sel = positions <= limits[i]
+        O[i], LSE[i] = attention(q[i], np.asarray(K)[sel], np.asarray(V)[sel], scale)
+    return O, LSE
+
+
+def mtp_query(wl, b: int, q_len: int, seed=None) -> np.ndarray:
+    """The ``q_len`` query rows of request ``b``: [q_len, H, Dqk]; query ``i`` is logical
+    query row ``b * q_len + i`` (so ``q_len = 1`` gives the single-token query)."""
+    seed = wl.seed if seed is None else seed
+    return np.stack([_query(wl, b * q_len + i, seed) for i in range(q_len)])
+
+
+def mtp_rank_partial(wl, b: int, rank: int, q_len: int, seed=None):
+    """(O_r [Q,H,Dv], LSE_r [Q,H]) of request ``b``'s ``q_len`` queries on ``rank``."""
+    seed = wl.seed if seed is None else seed
+    L = int(wl.lengths[b])
+    toks = rank_tokens(L, wl.dcp_size, wl.interleave, rank)
+    _, K, V = request_inputs(wl, b, toks, seed)
+    return causal_attention(mtp_query(wl, b, q_len, seed), K, V, toks, causal_limits(L, q_len),
+                            wl.softmax_scale)
+
+
+def mtp_full_attention(wl, b: int, q_len: int, seed=None):
+    """(O [Q,H,Dv], LSE [Q,H]) of request ``b``'s ``q_len`` queries over its whole context."""
+    seed = wl.seed if seed is None else seed
+    L = int(wl.lengths[b])
+    toks = np.arange(L, dtype=np.int64)
+    _, K, V = request_inputs(wl, b, toks, seed)
+    return causal_attention(mtp_query(wl, b, q_len, seed), K, V, toks, causal_limits(L, q_len),
+                            wl.softmax_scale)

@@ -47,10 +47,13 @@ def _rand_case(rng, H=8, Hkv=2, L=37, D=24, Dv=16):
 
 class Impl:
     def __init__(self, attention=oracle.attention, merge=oracle.merge,
-                 rank_tokens=oracle.rank_tokens):
+                 rank_tokens=oracle.rank_tokens, causal_attention=oracle.causal_attention,
+                 causal_limits=oracle.causal_limits):
         self.attention = attention
         self.merge = merge
         self.rank_tokens = rank_tokens
+        self.causal_attention = causal_attention
+        self.causal_limits = causal_limits
 
 
 # ----------------------------------------------------------------------------- pins
@@ -232,9 +235,91 @@ def check_large_logits(impl):
     assert np.allclose(Om, O, rtol=1e-10, atol=1e-12) and np.allclose(Lm, LSE, rtol=1e-13)
 
 
+def _mtp_case(rng, Q=3, H=4, Hkv=2, L=23, D=12, Dv=8):
+    q = rng.standard_normal((Q, H, D))
+    K = rng.standard_normal((L, Hkv, D))
+    V = rng.standard_normal((L, Hkv, Dv))
+    return q, K, V, 1.0 / math.sqrt(D)
+
+
+def check_mtp_single_query_is_decode(impl):
+    """One query token: the causal path is the single-token decode over every cached token."""
+    rng = np.random.default_rng(11)
+    q, K, V, sc = _mtp_case(rng, Q=1)
+    L = K.shape[0]
+    O, LSE = impl.causal_attention(q, K, V, np.arange(L), impl.causal_limits(L, 1), sc)
+    O1, L1 = impl.attention(q[0], K, V, sc)
+    assert np.allclose(O[0], O1, rtol=1e-13, atol=1e-14) and np.allclose(LSE[0], L1, atol=1e-13)
+
+
+def check_mtp_brute_force(impl):
+    """Multi-token queries against pure-Python loops: query i (the request's position
+    L - Q + i) sums over the tokens at positions <= L - Q + i."""
+    rng = np.random.default_rng(12)
+    q, K, V, sc = _mtp_case(rng, Q=4, H=4, Hkv=2, L=9, D=5, Dv=3)
+    Q, H, L = q.shape[0], q.shape[1], K.shape[0]
+    pos = np.arange(L)
+    O, LSE = impl.causal_attention(q, K, V, pos, impl.causal_limits(L, Q), sc)
+    G = H // K.shape[1]
+    for i in range(Q):
+        last = L - Q + i
+        for h in range(H):
+            g = h // G
+            s = [sc * sum(q[i, h, d] * K[t, g, d] for d in range(q.shape[2])) for t in range(last + 1)]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            tot = sum(w)
+            assert abs(LSE[i, h] - (m + math.log(tot))) < 1e-12
+            for e in range(V.shape[2]):
+                ref = sum(w[t] * V[t, g, e] for t in range(last + 1)) / tot
+                assert abs(O[i, h, e] - ref) < 1e-12
+
+
+def check_mtp_closed_form_counts(impl):
+    """q = 0 on rank r's tokens: query i sees exactly the rank's tokens among positions
+    0..L-Q+i, i.e. rank_length(L-Q+i+1) of them (the per-length formula of the pages'
+    1/N split, computed independently of the enumeration); LSE = ln(count) and O is the
+    running mean of V over them."""
+    N, I, Q = 3, 4, 5
+    for L in (1, 3, 11, 12, 13, 40):
+        for r in range(N):
+            toks = impl.rank_tokens(L, N, I, r)
+            T = len(toks)
+            V = np.arange(T * 2, dtype=np.float64).reshape(T, 1, 2)
+            K = np.ones((T, 1, 3))
+            q = np.zeros((Q, 2, 3))
+            O, LSE = impl.causal_attention(q, K, V, toks, impl.causal_limits(L, Q), 0.5)
+            for i in range(Q):
+                n_vis = oracle.rank_length(max(L - Q + i + 1, 0), N, I, r)
+                if n_vis == 0:
+                    assert np.all(np.isneginf(LSE[i])) and np.all(O[i] == 0)
+                    continue
+                assert np.allclose(LSE[i], math.log(n_vis), atol=1e-13)
+                mean = np.cumsum(V[:, 0, :], axis=0)[n_vis - 1] / n_vis
+                assert np.allclose(O[i], mean[None, :], atol=1e-12)
+
+
+def check_mtp_sharded_merge_equals_unsharded(impl):
+    """Blog Sec. 4.1 with causal multi-token queries: the ranks' causal partials merge
+    to the unsharded causal attention, for several N and I."""
+    rng = np.random.default_rng(13)
+    q, K, V, sc = _mtp_case(rng, Q=3, L=29)
+    L, Q = K.shape[0], q.shape[0]
+    Ou, Lu = impl.causal_attention(q, K, V, np.arange(L), impl.causal_limits(L, Q), sc)
+    for N, I in ((2, 1), (3, 4), (4, 2), (5, 16)):
+        parts = []
+        for r in range(N):
+            toks = impl.rank_tokens(L, N, I, r)
+            parts.append(impl.causal_attention(q, K[toks], V[toks], toks, impl.causal_limits(L, Q), sc))
+        O, LSE = impl.merge([p[0] for p in parts], [p[1] for p in parts])
+        assert np.allclose(O, Ou, rtol=1e-12, atol=1e-13) and np.allclose(LSE, Lu, atol=1e-13)
+
+
 ALL_CHECKS = [check_contiguous_example, check_one_nth, check_partition, check_against_torch_sdpa,
               check_closed_forms, check_brute_force, check_merge_equals_unsharded,
-              check_merge_identities, check_large_logits]
+              check_merge_identities, check_large_logits, check_mtp_single_query_is_decode,
+              check_mtp_brute_force, check_mtp_closed_form_counts,
+              check_mtp_sharded_merge_equals_unsharded]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -313,6 +398,27 @@ def _mut_tokens(kind):
     return toks
 
 
+def _mut_causal(kind):
+    def causal(q, K, V, positions, limits, scale):
+        positions = np.asarray(positions)
+        if kind == "strict":
+            limits = np.asarray(limits) - 1
+        if kind == "local_index":  # masks by the rank-local index instead of the position
+            positions = np.arange(len(positions))
+        if kind == "query_reversed":
+            limits = np.asarray(limits)[::-1]
+        return oracle.causal_attention(q, K, V, positions, limits, scale)
+    return causal
+
+
+def _mut_limits(kind):
+    def lim(L, q_len):
+        if kind == "shift":
+            return L - q_len + 1 + np.arange(q_len)
+        return L - 1 - np.arange(q_len)[::-1] * 0  # every query sees everything
+    return lim
+
+
 MUTANTS = (
     [("attention:" + k, Impl(attention=_mut_attention(k))) for k in
      ["group_mod", "no_scale", "sign", "v_offset", "unnormalised", "lse_no_max", "lse_log2", "drop_last"]]
@@ -320,6 +426,9 @@ MUTANTS = (
        ["uniform_weights", "lse_max_only", "no_renorm", "empty_nan"]]
     + [("tokens:" + k, Impl(rank_tokens=_mut_tokens(k))) for k in
        ["mod_first", "block_by_n", "off_by_one"]]
+    + [("causal:" + k, Impl(causal_attention=_mut_causal(k))) for k in
+       ["strict", "local_index", "query_reversed"]]
+    + [("limits:" + k, Impl(causal_limits=_mut_limits(k))) for k in ["shift", "no_mask"]]
 )
 
 
