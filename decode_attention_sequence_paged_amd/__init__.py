@@ -63,6 +63,9 @@ _SIGS = {
     "dcp_append_kv": (_i32, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp,
                              _i32, _i32, _i32, _i32, _vp]),
     "dcp_merge_lse": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "dcp_decode_workspace_size_mtp": (_sz, [ctypes.POINTER(AttnDesc), _i32, _i32, _i32]),
+    "dcp_decode_partial_mtp": (_i32, [ctypes.POINTER(AttnDesc), _i32, _vp, _vp, _vp, _i64, _vp, _i32,
+                                      _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "dcp_rescale_partial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "dcp_sum_head_slice": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
 }
@@ -217,6 +220,23 @@ def dcp_sum_head_slice(scaled_parts, rank: int, out, stream=None) -> None:
     dt = DCP_DTYPE_BF16 if scaled_parts.dtype == _torch().bfloat16 else DCP_DTYPE_F32
     _check("dcp_sum_head_slice", lib().dcp_sum_head_slice(
         _dptr(scaled_parts), dt, N, B, H, Dv, rank, _dptr(out), _stream(stream)))
+
+
+def dcp_decode_workspace_size_mtp(desc: AttnDesc, q_len: int, batch: int, num_partitions: int = 0) -> int:
+    return int(lib().dcp_decode_workspace_size_mtp(ctypes.byref(desc), q_len, batch, num_partitions))
+
+
+def dcp_decode_partial_mtp(desc: AttnDesc, q, k_cache, v_cache, block_table, seq_lens, rank: int,
+                           num_ranks: int, interleave: int, workspace, out_o, out_lse,
+                           num_partitions: int = 0, stream=None) -> None:
+    """One rank's partial attention for q_len query tokens per request, causal by global
+    position: q [B, q_len, H, qk_dim]; out_o [B, q_len, H, v_dim]; out_lse [B, q_len, H]."""
+    batch, q_len = q.shape[0], q.shape[1]
+    _check("dcp_decode_partial_mtp", lib().dcp_decode_partial_mtp(
+        ctypes.byref(desc), q_len, _dptr(q), _dptr(k_cache), _dptr(v_cache), k_cache.shape[0],
+        _dptr(block_table), block_table.shape[1], _dptr(seq_lens), batch, rank, num_ranks,
+        interleave, num_partitions, _dptr(workspace), workspace.numel() * workspace.element_size(),
+        _dptr(out_o), _dptr(out_lse), _stream(stream)))
 
 
 def dcp_merge(o_parts, lse_parts, out_o, out_lse, stream=None) -> None:

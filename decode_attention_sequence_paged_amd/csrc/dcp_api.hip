@@ -15,6 +15,8 @@ namespace {
 
 constexpr int32_t kMaxBatch = 1 << 16;
 constexpr int32_t kMaxParts = 1 << 16;
+constexpr int32_t kMaxMlaRows = 512;  // MLA score rows (query tokens x heads) per request
+constexpr int64_t kMaxMtpRows = kMaxMlaRows;
 constexpr int32_t kMaxDevices = 64;
 
 // Read-only cache of the compute-unit count per device (filled on first use).
@@ -43,7 +45,7 @@ dcp_status_t check_desc(const dcp_attn_desc_t* d, int32_t* head_groups) {
   if (d->kind == DCP_KV_MLA_LATENT) {
     if (d->num_kv_heads != 1) return DCP_ERROR_INVALID_VALUE;
     if (d->qk_dim != 576 || d->v_dim != 512) return DCP_ERROR_NOT_SUPPORTED;
-    if (d->num_q_heads > 128 || d->block_size % dcp::kMlaTile) return DCP_ERROR_NOT_SUPPORTED;
+    if (d->num_q_heads > kMaxMlaRows || d->block_size % dcp::kMlaTile) return DCP_ERROR_NOT_SUPPORTED;
     const int hpg = dcp::mla_heads_per_group(d->num_q_heads);
     *head_groups = (d->num_q_heads + hpg - 1) / hpg;
     return DCP_SUCCESS;
@@ -86,6 +88,18 @@ WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
   l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);
   return l;
+}
+
+// Multi-token decode queries: q_len query tokens of num_q_heads heads become
+// q_len * num_q_heads score rows (MLA only).
+dcp_status_t check_q_len(const dcp_attn_desc_t* d, int32_t q_len, dcp_attn_desc_t* rows) {
+  *rows = *d;
+  if (q_len < 1) return DCP_ERROR_INVALID_VALUE;
+  if (q_len == 1) return DCP_SUCCESS;
+  if (d->kind != DCP_KV_MLA_LATENT) return DCP_ERROR_NOT_SUPPORTED;
+  if (d->num_q_heads < 1 || (int64_t)q_len * d->num_q_heads > kMaxMtpRows) return DCP_ERROR_NOT_SUPPORTED;
+  rows->num_q_heads = q_len * d->num_q_heads;
+  return DCP_SUCCESS;
 }
 
 dcp_status_t check_shard_args(int32_t num_ranks, int32_t interleave, int32_t rank) {
@@ -184,23 +198,35 @@ dcp_status_t dcp_local_block_table(const int32_t* global_block_table, int32_t ba
                                                   (hipStream_t)stream));
 }
 
-size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch, int32_t num_partitions) {
+size_t dcp_decode_workspace_size_mtp(const dcp_attn_desc_t* desc, int32_t q_len, int32_t batch,
+                                     int32_t num_partitions) {
+  dcp_attn_desc_t d;
+  if (!desc || check_q_len(desc, q_len, &d) != DCP_SUCCESS) return 0;
   int32_t groups = 0;
-  if (check_desc(desc, &groups) != DCP_SUCCESS) return 0;
+  if (check_desc(&d, &groups) != DCP_SUCCESS) return 0;
   if (batch < 0 || batch > kMaxBatch || num_partitions < 0 || num_partitions > kMaxParts) return 0;
   const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
-  return ws_layout(batch, parts, desc->num_q_heads, desc->v_dim).total;
+  return ws_layout(batch, parts, d.num_q_heads, d.v_dim).total;
 }
 
-dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
-                                const void* v_cache, int64_t num_cache_blocks,
-                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                                const int32_t* seq_lens, int32_t batch, int32_t rank,
-                                int32_t num_ranks, int32_t interleave, int32_t num_partitions,
-                                void* workspace, size_t workspace_bytes, float* out_o,
-                                float* out_lse, void* stream) {
+size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch, int32_t num_partitions) {
+  return dcp_decode_workspace_size_mtp(desc, 1, batch, num_partitions);
+}
+
+dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    int64_t num_cache_blocks, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                    int32_t batch, int32_t rank, int32_t num_ranks,
+                                    int32_t interleave, int32_t num_partitions, void* workspace,
+                                    size_t workspace_bytes, float* out_o, float* out_lse,
+                                    void* stream) {
+  if (!desc) return DCP_ERROR_INVALID_VALUE;
+  dcp_attn_desc_t d;  // one score row per (query token, head)
+  dcp_status_t st = check_q_len(desc, q_len, &d);
+  if (st != DCP_SUCCESS) return st;
   int32_t groups = 0;
-  dcp_status_t st = check_desc(desc, &groups);
+  st = check_desc(&d, &groups);
   if (st != DCP_SUCCESS) return st;
   st = check_shard_args(num_ranks, interleave, rank);
   if (st != DCP_SUCCESS) return st;
@@ -210,11 +236,11 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   if (batch == 0) return DCP_SUCCESS;
   if (!q || !k_cache || !block_table || !seq_lens || !out_o || !out_lse) return DCP_ERROR_INVALID_VALUE;
   if (num_cache_blocks < 1 || max_blocks_per_seq < 1) return DCP_ERROR_INVALID_VALUE;
-  if ((desc->kind == DCP_KV_MLA_LATENT) != (v_cache == nullptr)) return DCP_ERROR_INVALID_VALUE;
+  if ((d.kind == DCP_KV_MLA_LATENT) != (v_cache == nullptr)) return DCP_ERROR_INVALID_VALUE;
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return DCP_ERROR_INVALID_VALUE;
   if (((uintptr_t)out_o & 15) || ((uintptr_t)out_lse & 3)) return DCP_ERROR_INVALID_VALUE;
   const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
-  const WsLayout wl = ws_layout(batch, parts, desc->num_q_heads, desc->v_dim);
+  const WsLayout wl = ws_layout(batch, parts, d.num_q_heads, d.v_dim);
   if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < wl.total) return DCP_ERROR_WORKSPACE;
 
   uint8_t* ws = (uint8_t*)workspace;
@@ -226,21 +252,23 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   p.block_table = block_table;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.batch = batch;
-  p.num_q_heads = desc->num_q_heads;
-  p.num_kv_heads = desc->num_kv_heads;
-  p.block_size = desc->block_size;
+  p.num_q_heads = d.num_q_heads;
+  p.num_kv_heads = d.num_kv_heads;
+  p.block_size = d.block_size;
   p.num_head_groups = groups;
-  p.scale_log2 = desc->softmax_scale * 1.4426950408889634f;
+  p.q_len = q_len;
+  p.heads_per_token = desc->num_q_heads;
+  p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   p.part.seq_lens = seq_lens;
   p.part.batch = batch;
   p.part.rank = rank;
   p.part.num_ranks = num_ranks;
   p.part.interleave = interleave;
   p.part.max_blocks_per_seq = max_blocks_per_seq;
-  p.part.block_size = desc->block_size;
-  p.part.tile = desc->kind == DCP_KV_MLA_LATENT ? dcp::kMlaTile : dcp::kGqaTile;
+  p.part.block_size = d.block_size;
+  p.part.tile = d.kind == DCP_KV_MLA_LATENT ? dcp::kMlaTile : dcp::kGqaTile;
   p.part.num_parts = parts;
-  p.part.req_weight = request_weight(desc);
+  p.part.req_weight = request_weight(&d);
   p.out_o = out_o;
   p.out_lse = out_lse;
   p.ws_prefix = (int64_t*)(ws + wl.prefix);
@@ -248,8 +276,8 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   p.ws_o = (float*)(ws + wl.o);
 
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = desc->kind == DCP_KV_MLA_LATENT ? dcp::launch_mla_partial(p, s)
-                                                 : dcp::launch_gqa_partial(p, s);
+  hipError_t e = d.kind == DCP_KV_MLA_LATENT ? dcp::launch_mla_partial(p, s)
+                                             : dcp::launch_gqa_partial(p, s);
   if (e != hipSuccess) return DCP_ERROR_HIP;
 
   dcp::SplitReduceParams r{};
@@ -257,13 +285,25 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
   r.ws_lse = p.ws_lse;
   r.ws_o = p.ws_o;
   r.batch = batch;
-  r.num_heads = desc->num_q_heads;
-  r.v_dim = desc->v_dim;
+  r.num_heads = d.num_q_heads;
+  r.v_dim = d.v_dim;
   r.num_parts = parts;
   r.req_weight = p.part.req_weight;
   r.out_o = out_o;
   r.out_lse = out_lse;
   return hip_status(dcp::launch_split_reduce(r, s));
+}
+
+dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_cache_blocks,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t batch, int32_t rank,
+                                int32_t num_ranks, int32_t interleave, int32_t num_partitions,
+                                void* workspace, size_t workspace_bytes, float* out_o,
+                                float* out_lse, void* stream) {
+  return dcp_decode_partial_mtp(desc, 1, q, k_cache, v_cache, num_cache_blocks, block_table,
+                                max_blocks_per_seq, seq_lens, batch, rank, num_ranks, interleave,
+                                num_partitions, workspace, workspace_bytes, out_o, out_lse, stream);
 }
 
 dcp_status_t dcp_append_kv(const dcp_attn_desc_t* desc, const void* new_k, const void* new_v,

@@ -236,11 +236,14 @@ constexpr int kTileTokens = 32;  // tokens per streamed tile (both kernels)
 // and the tile starts at token kTileTokens * sub of that page (tpp tiles per page).
 struct Cursor {
   int b, t, ntile, Lr, pk, sub;
+  int Lg;  // the request's global length
   const int32_t* bt_row;
 };
 
 __device__ __forceinline__ void cursor_request(Cursor& c, const PartialParams& p, int b) {
   c.b = b;
+  const int32_t L = ld_const(p.part.seq_lens + b);
+  c.Lg = L < 0 ? 0 : L;
   c.Lr = (int)part_local_len(p.part, b);
   c.ntile = (c.Lr + kTileTokens - 1) / kTileTokens;
   c.bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
@@ -277,6 +280,27 @@ __device__ __forceinline__ float sum_over_groups(float x) {
   x = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
   auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+// Causal mask of multi-token decode queries: the q_len queries are the request's last
+// q_len positions, and query i (score row `row`, i = row / heads_per_token) sees the
+// global positions <= Lg - q_len + i.  Masks this lane's eight scores (tokens 4 q4 + e
+// and 16 + 4 q4 + e of the tile at cursor `cur`); tiles whose last token every query
+// sees are left alone after one wave-uniform test.
+__device__ __forceinline__ void causal_mask(const PartialParams& p, const Cursor& cur, int nvalid,
+                                            int row, int q4, f32x4& s0, f32x4& s1) {
+  if (p.q_len <= 1) return;
+  const int N = p.part.num_ranks, I = p.part.interleave, r = p.part.rank;
+  const int64_t j0 = (int64_t)cur.t * kTileTokens;
+  const int64_t last = j0 + (nvalid < kTileTokens ? nvalid : kTileTokens) - 1;
+  const int64_t lim0 = (int64_t)cur.Lg - p.q_len;
+  if (dcp_global_index(last, N, I, r) <= lim0) return;
+  const int64_t lim = lim0 + row / p.heads_per_token;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (dcp_global_index(j0 + 4 * q4 + e, N, I, r) > lim) s0[e] = -INFINITY;
+    if (dcp_global_index(j0 + 16 + 4 * q4 + e, N, I, r) > lim) s1[e] = -INFINITY;
+  }
 }
 
 // s_waitcnt lgkmcnt(0) as a builtin, so the compiler's own wait counting knows every

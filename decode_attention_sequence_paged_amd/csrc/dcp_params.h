@@ -25,6 +25,8 @@ struct PartialParams {
   int32_t max_blocks_per_seq;
   int32_t batch, num_q_heads, num_kv_heads, block_size;
   int32_t num_head_groups;  // work-groups sharing one span (disjoint head sets)
+  int32_t q_len;            // query tokens per request (1: single-token decode)
+  int32_t heads_per_token;  // query heads per query token; rows = q_len * heads_per_token
   float scale_log2;         // softmax_scale * log2(e)
   PartitionArgs part;
   float* out_o;             // [B, H, v_dim]

@@ -265,12 +265,14 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
                        fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mloc = max_over_groups(mloc);
     const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
-    alpha = fast_exp2(m_run - m_new);
+    // no visible token yet (a causally masked row): nothing to weigh or rescale
+    const bool none = m_new == -INFINITY;
+    alpha = none ? 1.f : fast_exp2(m_run - m_new);
     moved = m_new != m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pr = fast_exp2(x[j] - m_new);
+      const float pr = none ? 0.f : fast_exp2(x[j] - m_new);
       lsum += pr;
       pb[j] = (__bf16)pr;
     }
@@ -408,6 +410,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
         if (16 + 4 * q4 + j >= nvalid) s1[j] = -INFINITY;
       }
     }
+    causal_mask(p, cur, nvalid, head, q4, s0, s1);
     softmax(s0, s1);
     if (__any(moved)) {
 #pragma unroll
@@ -423,8 +426,9 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
       const bool whole = piece_t0 == 0 && last_of_req;
       const int64_t slot = 2 * w + (first_piece ? 0 : 1);
       pend = true;
-      pend_inv = 1.0f / l_run;
-      pend_lse = (m_run + fast_log2(l_run)) * kLn2;
+      // a row that saw no token of the piece: O = 0, LSE = -inf
+      pend_inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      pend_lse = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
       const int hd = head < H ? head : 0;
       pend_o = (whole ? p.out_o + ((int64_t)cur.b * H + hd) * kDv : p.ws_o + (slot * H + hd) * kDv) + 4 * q4;
       pend_l = whole ? p.out_lse + (int64_t)cur.b * H + hd : p.ws_lse + slot * H + hd;
@@ -604,6 +608,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
           if (16 + 4 * q4 + e >= nvalid) s1[e] = -INFINITY;
         }
       }
+      causal_mask(p, cur, nvalid, head, q4, s0, s1);
       // online softmax over the tile's 32 scores of this lane's head (lazy rescale)
       float x[8];
 #pragma unroll
@@ -612,12 +617,14 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
       mloc = max_over_groups(mloc);
       const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
+      // no visible token yet (a causally masked row): nothing to weigh or rescale
+      const bool none = m_new == -INFINITY;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
       bf16x8 pb;
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pr = fast_exp2(x[e] - m_new);
+        const float pr = none ? 0.f : fast_exp2(x[e] - m_new);
         lsum += pr;
         pb[e] = (__bf16)pr;
       }
@@ -630,8 +637,10 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
         bool whole;
         const int64_t row = piece_row(pc, cur, head_ok ? head : 0, whole);
         if (q4 == 0) {
-          s_inv[par][l16][sb] = 1.0f / l_run;
-          if (head_ok) (whole ? p.out_lse : p.ws_lse)[row] = (m_run + fast_log2(l_run)) * kLn2;
+          // a row that saw no token of the piece: O = 0, LSE = -inf
+          s_inv[par][l16][sb] = l_run > 0.f ? 1.0f / l_run : 0.f;
+          if (head_ok)
+            (whole ? p.out_lse : p.ws_lse)[row] = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
         }
         pc.t0 = 0;
         pc.first = false;

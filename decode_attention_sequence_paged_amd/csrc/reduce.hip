@@ -101,7 +101,9 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
         for (int u = 0; u < C::kUnroll; ++u) {
           const int i = i0 + u * PL;
           const int64_t slot = i < cnt ? s_slot[i] : -1;
-          wt[u] = slot >= 0 ? fast_exp2(s_lse[i][hd] - mx) : 0.f;
+          // empty pieces (a causally masked row) carry no weight
+          const float l = s_lse[i][hd];
+          wt[u] = slot >= 0 && l != -INFINITY ? fast_exp2(l - mx) : 0.f;
           v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * q) : f32x4{};
         }
 #pragma unroll
@@ -125,8 +127,9 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
     }
   }
   if (!head_ok) return;
-  *(f32x4*)orow = acc * (1.0f / wsum);
-  if (q == 0) p.out_lse[(int64_t)b * H + head] = (mx + fast_log2(wsum)) * kLn2;
+  // a row no piece saw a token for: the merge's neutral element
+  *(f32x4*)orow = wsum > 0.f ? acc * (1.0f / wsum) : f32x4{};
+  if (q == 0) p.out_lse[(int64_t)b * H + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int DV, int PL>

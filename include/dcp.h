@@ -166,7 +166,7 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *   out_lse      device fp32 [batch, H], written: LSE_r = ln sum_t exp(s_t),
  *                s_t = softmax_scale * (q . k_t).
  *   A request with no local tokens gets O_r = 0 and LSE_r = -inf.
- * Supported: MLA with qk_dim 576, v_dim 512, 1 <= H <= 128, block_size a
+ * Supported: MLA with qk_dim 576, v_dim 512, 1 <= H <= 512, block_size a
  * multiple of 32; GQA with qk_dim = v_dim = 128, H / num_kv_heads <= 16,
  * block_size a multiple of 16.
  * Errors: INVALID_VALUE, NOT_SUPPORTED, WORKSPACE, HIP (nothing runs on error). */
@@ -177,6 +177,33 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
                                 int32_t num_ranks, int32_t interleave, int32_t num_partitions,
                                 void* workspace, size_t workspace_bytes, float* out_o,
                                 float* out_lse, void* stream);
+
+/* Multi-token decode queries (speculative decoding / multi-token prediction; blog
+ * Sec. 6): q_len >= 1 query tokens per request, the request's last q_len positions,
+ * whose K/V rows are already in the cache (seq_lens counts them).  Query i (global
+ * position L - q_len + i) attends the positions <= L - q_len + i, causally by GLOBAL
+ * position, so on each rank it sees the local tokens up to that position; a query
+ * that sees none of the rank's tokens gets O_r = 0, LSE_r = -inf, and dcp_merge over
+ * the ranks gives causal attention over the whole context.  q_len = 1 is
+ * dcp_decode_partial.
+ *   q        device bf16 [batch, q_len, H, qk_dim]
+ *   out_o    device fp32 [batch, q_len, H, v_dim], written
+ *   out_lse  device fp32 [batch, q_len, H], written
+ *   workspace  >= dcp_decode_workspace_size_mtp(desc, q_len, batch, num_partitions)
+ * Every other argument as for dcp_decode_partial.
+ * Supported: MLA with q_len * H <= 512 (GQA: q_len = 1 only, else NOT_SUPPORTED).
+ * Errors: INVALID_VALUE (q_len < 1, and as dcp_decode_partial), NOT_SUPPORTED,
+ * WORKSPACE, HIP (nothing runs on error).                                      */
+size_t dcp_decode_workspace_size_mtp(const dcp_attn_desc_t* desc, int32_t q_len, int32_t batch,
+                                     int32_t num_partitions);
+dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, const void* q,
+                                    const void* k_cache, const void* v_cache,
+                                    int64_t num_cache_blocks, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                    int32_t batch, int32_t rank, int32_t num_ranks,
+                                    int32_t interleave, int32_t num_partitions, void* workspace,
+                                    size_t workspace_bytes, float* out_o, float* out_lse,
+                                    void* stream);
 
 /* ------------------------------------------------------------------ KV append
  * Blog Sec. 4 ("What is DCP?") and Sec. 2.2: every rank stores the KV of its own

@@ -85,7 +85,7 @@ def test_workspace_size_and_desc_validation():
     bad = [
         dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 2, 576, 512, 128, 0.1),   # MLA has one KV head
         dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 512, 512, 128, 0.1),   # unsupported dims
-        dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 256, 1, 576, 512, 128, 0.1),  # too many heads
+        dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 1024, 1, 576, 512, 128, 0.1),  # too many heads
         dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 48, 0.1),    # page not a tile multiple
         dcp.attn_desc(dcp.DCP_KV_GQA, 64, 3, 128, 128, 16, 0.1),           # H % Hkv != 0
         dcp.attn_desc(dcp.DCP_KV_GQA, 64, 2, 128, 128, 16, 0.1),           # group of 32 > 16
@@ -168,3 +168,25 @@ def test_merge_steps_reject_bad_arguments_before_launching():
     assert lib.dcp_sum_head_slice(fake, 5, 4, 2, 64, 512, 0, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
     assert lib.dcp_sum_head_slice(fake + 4, BF16, 4, 2, 64, 512, 0, fake, 0) == dcp.DCP_ERROR_INVALID_VALUE
     assert lib.dcp_sum_head_slice(fake, BF16, 4, 0, 64, 512, 0, fake, 0) == dcp.DCP_SUCCESS
+
+
+def test_mtp_entry_point_validation():
+    import ctypes
+    lib = dcp.lib()
+    mla = dcp.attn_desc(dcp.DCP_KV_MLA_LATENT, 64, 1, 576, 512, 128, 0.05)
+    gqa = dcp.attn_desc(dcp.DCP_KV_GQA, 64, 4, 128, 128, 16, 0.05)
+    assert dcp.dcp_decode_workspace_size_mtp(mla, 1, 4, 8) == dcp.dcp_decode_workspace_size(mla, 4, 8)
+    assert dcp.dcp_decode_workspace_size_mtp(mla, 4, 4, 8) > dcp.dcp_decode_workspace_size(mla, 4, 8)
+    assert dcp.dcp_decode_workspace_size_mtp(mla, 0, 4, 8) == 0
+    assert dcp.dcp_decode_workspace_size_mtp(mla, 9, 4, 8) == 0      # 9 x 64 rows > 512
+    assert dcp.dcp_decode_workspace_size_mtp(gqa, 2, 4, 8) == 0      # GQA: one query token only
+    assert dcp.dcp_decode_workspace_size_mtp(gqa, 1, 4, 8) > 0
+    fake = 1 << 20
+    def call(desc=mla, q_len=2, B=2, rank=0):
+        return lib.dcp_decode_partial_mtp(ctypes.byref(desc), q_len, fake, fake, 0, 10, fake, 4, fake, B,
+                                          rank, 2, 1, 8, fake * 2, 1 << 30, fake, fake, 0)
+    assert call(q_len=0) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(q_len=9) == dcp.DCP_ERROR_NOT_SUPPORTED
+    assert call(desc=gqa) == dcp.DCP_ERROR_NOT_SUPPORTED
+    assert call(rank=2) == dcp.DCP_ERROR_INVALID_VALUE
+    assert call(B=0) == dcp.DCP_SUCCESS

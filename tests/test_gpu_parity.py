@@ -29,6 +29,8 @@ def _paged():
 def _wl(name, **kw):
     base = di.WORKLOADS[name]
     d = dict(base.__dict__)
+    if "lengths" in kw and "batch" not in kw:
+        kw = dict(kw, batch=len(kw["lengths"]))
     d.update(kw)
     return di.Workload(**d)
 
@@ -490,3 +492,95 @@ def test_merge_decomposition_equals_fused_merge(name, kw):
         for dtype, o in outs.items():
             check_close(o[b].cpu().numpy()[None], ld[b][None], o_ref[None], l_ref[None],
                         "decomposed merge (%s) b=%d" % (dtype, b))
+
+
+# ----------------------------------------------------------------------------- multi-token queries
+
+def run_rank_mtp(wl, rank, q_len, census=False, parts=0):
+    """One rank's partial for q_len query tokens per request through dcp_decode_partial_mtp.
+    Query i of request b is logical query row b * q_len + i."""
+    pg = _paged()
+    B, H = wl.batch, wl.num_q_heads
+    rc = pg.build_rank_cache(wl, rank, census=census, lengths=np.asarray(wl.lengths))
+    q = pg.device_query(_wl(wl.name, batch=B * q_len, seed=wl.seed), census=census).view(B, q_len, H, wl.qk_dim)
+    sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+    desc = pg.desc_for(wl)
+    ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(desc, q_len, B, parts), dtype=torch.uint8, device="cuda")
+    o = torch.full((B, q_len, H, wl.v_dim), float("nan"), device="cuda")
+    lse = torch.full((B, q_len, H), float("nan"), device="cuda")
+    dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl, rank, wl.dcp_size,
+                               wl.interleave, ws, o, lse, num_partitions=parts)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+MTP_CASES = [
+    ("mla_tiny", 2, dict()),
+    ("mla_tiny", 4, dict(dcp_size=3, interleave=5, block_size=32, lengths=(1000, 3000, 1, 2, 3, 17))),
+    ("mla_tiny", 3, dict(dcp_size=4, interleave=2, lengths=(7, 9, 2049, 64))),
+    ("mla_long_b128", 2, dict(batch=3, lengths=(5000, 20000, 1030))),
+    ("mla_long_b128", 4, dict(batch=2, lengths=(3000, 1025))),
+]
+
+
+@pytest.mark.parametrize("name,q_len,kw", MTP_CASES)
+@pytest.mark.parametrize("parts", [0, 5])
+def test_mtp_every_rank_and_merge(name, q_len, kw, parts):
+    """Multi-token decode queries, causal by global position: each rank's partials
+    against the oracle's causal partials (including queries that see none of a rank's
+    tokens), and the merge over the ranks against causal attention over the whole
+    context."""
+    wl = _wl(name, **kw)
+    N, B, H, Dv = wl.dcp_size, wl.batch, wl.num_q_heads, wl.v_dim
+    o_all = torch.empty((N, B, q_len * H, Dv), device="cuda")
+    l_all = torch.empty((N, B, q_len * H), device="cuda")
+    for r in range(N):
+        o, lse = run_rank_mtp(wl, r, q_len, parts=parts)
+        o_all[r] = o.view(B, q_len * H, Dv)
+        l_all[r] = lse.view(B, q_len * H)
+        on, ln = o.cpu().numpy(), lse.cpu().numpy()
+        for b in range(B):
+            o_ref, l_ref = oracle.mtp_rank_partial(wl, b, r, q_len)
+            check_close(on[b], ln[b], o_ref, l_ref, "mtp rank %d b=%d" % (r, b))
+    om = torch.empty((B, q_len * H, Dv), device="cuda")
+    lm = torch.empty((B, q_len * H), device="cuda")
+    dcp.dcp_merge(o_all, l_all, om, lm)
+    torch.cuda.synchronize()
+    om, lm = om.view(B, q_len, H, Dv).cpu().numpy(), lm.view(B, q_len, H).cpu().numpy()
+    for b in range(B):
+        o_ref, l_ref = oracle.mtp_full_attention(wl, b, q_len)
+        check_close(om[b], lm[b], o_ref, l_ref, "mtp merged b=%d" % b)
+
+
+def test_mtp_single_query_is_the_decode_call():
+    """q_len = 1 through the multi-token entry point is the single-token call, bit for bit."""
+    wl = _wl("mla_tiny", dcp_size=3, interleave=5)
+    for r in range(wl.dcp_size):
+        o1, l1, _ = run_rank(wl, r)
+        o2, l2 = run_rank_mtp(wl, r, 1)
+        assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
+
+
+@pytest.mark.parametrize("q_len,kw", [(4, dict(dcp_size=3, interleave=5, block_size=32,
+                                                lengths=(1000, 3000, 1, 2, 3, 17))),
+                                      (2, dict(dcp_size=2, interleave=1, lengths=(64, 65)))])
+def test_mtp_census(q_len, kw):
+    """q = 0 and V rows = bits of the global token id: for every query, O * count recovers
+    exactly how many of the tokens it may see (the rank's tokens at positions
+    <= L - q_len + i, enumerated by the oracle) have each bit set."""
+    wl = _wl("mla_tiny", **kw)
+    for r in range(wl.dcp_size):
+        o, lse = run_rank_mtp(wl, r, q_len, census=True)
+        o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+        for b in range(wl.batch):
+            L = int(wl.lengths[b])
+            toks = oracle.rank_tokens(L, wl.dcp_size, wl.interleave, r)
+            for i in range(q_len):
+                vis = toks[toks <= L - q_len + i]
+                if vis.size == 0:
+                    assert np.all(np.isneginf(lse[b, i])) and np.all(o[b, i] == 0), (r, b, i)
+                    continue
+                counts = np.array([((vis >> d) & 1).sum() for d in range(24)], dtype=np.float64)
+                got = np.rint(o[b, i][:, :24] * vis.size)
+                assert np.array_equal(got, np.broadcast_to(counts, got.shape)), (r, b, i)
+                assert np.allclose(lse[b, i], math.log(vis.size), atol=1e-4), (r, b, i)
