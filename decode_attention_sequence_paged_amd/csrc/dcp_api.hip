@@ -63,10 +63,10 @@ dcp_status_t check_desc(const dcp_attn_desc_t* d, int32_t* head_groups) {
 // helpers in dcp_device.h): the query slice it reads and the fp32 output row it
 // writes, in units of the tile bytes it streams.  MLA: a 64-head group moves 72 KiB
 // of q and 128 KiB of O against 36 KiB per tile (about 5.6; 5 measured), a 32-head
-// group half of that; GQA: 12 KiB against 16 KiB per KV head.
+// group half of that; GQA: 12 KiB per KV head against its 8 KiB of a 16-token tile.
 int32_t request_weight(const dcp_attn_desc_t* d) {
   if (d->kind == DCP_KV_MLA_LATENT) return dcp::mla_heads_per_group(d->num_q_heads) == 64 ? 5 : 3;
-  return 1;
+  return 2;
 }
 
 int32_t default_parts(int32_t head_groups) {

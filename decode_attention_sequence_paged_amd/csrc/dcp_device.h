@@ -84,6 +84,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Load through the constant address space: the data is read-only for the whole
 // kernel, so a wave-uniform address becomes a scalar load (counted by lgkmcnt, not
@@ -195,12 +200,14 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
   }
   if (prefix_out && tid == NT - 1) { prefix_out[a.batch] = TT; prefix_out[2 * a.batch + 1] = WT; }
   __syncthreads();
+  // Every lane read the same LDS values; say so, so that what the kernels derive from
+  // the span (loop bounds, page bases) stays in scalar registers.
   SpanLoc loc;
-  loc.total = TT;
-  loc.b0 = (int32_t)s_loc[0];
-  loc.off0 = s_loc[1];
-  loc.start = x0 < x1 ? s_loc[2] : 0;
-  loc.end = x0 < x1 ? (x1 >= WT ? TT : s_loc[3]) : 0;
+  loc.total = uniform64(TT);
+  loc.b0 = uniform((int32_t)s_loc[0]);
+  loc.off0 = uniform64(s_loc[1]);
+  loc.start = uniform64(x0 < x1 ? s_loc[2] : 0);
+  loc.end = uniform64(x0 < x1 ? (x1 >= WT ? TT : s_loc[3]) : 0);
   __syncthreads();  // s_loc / s_scan may be reused after this
   return loc;
 }
@@ -233,24 +240,27 @@ constexpr int kTileTokens = 32;  // tokens per streamed tile (both kernels)
 //
 // Position in a span's sequence of (request, tile) pairs, 32-bit and division free
 // inside the loops: the page of tile t is entry pk of the request's block-table row
-// and the tile starts at token kTileTokens * sub of that page (tpp tiles per page).
+// and the tile starts at token T * sub of that page (tpp tiles of T tokens per page;
+// T = kTileTokens unless a kernel streams other tiles).
 struct Cursor {
   int b, t, ntile, Lr, pk, sub;
   int Lg;  // the request's global length
   const int32_t* bt_row;
 };
 
+template <int T = kTileTokens>
 __device__ __forceinline__ void cursor_request(Cursor& c, const PartialParams& p, int b) {
   c.b = b;
   const int32_t L = ld_const(p.part.seq_lens + b);
   c.Lg = L < 0 ? 0 : L;
   c.Lr = (int)part_local_len(p.part, b);
-  c.ntile = (c.Lr + kTileTokens - 1) / kTileTokens;
+  c.ntile = (c.Lr + T - 1) / T;
   c.bt_row = p.block_table + (int64_t)b * p.max_blocks_per_seq;
 }
 
+template <int T = kTileTokens>
 __device__ __forceinline__ void cursor_set(Cursor& c, const PartialParams& p, int tpp, int b, int t) {
-  cursor_request(c, p, b);
+  cursor_request<T>(c, p, b);
   c.t = t;
   c.pk = t / tpp;
   c.sub = t - c.pk * tpp;
@@ -258,11 +268,12 @@ __device__ __forceinline__ void cursor_set(Cursor& c, const PartialParams& p, in
 
 // Advance to the next tile; only called while the span has tiles left, so a
 // non-empty request follows whenever the current one is exhausted.
+template <int T = kTileTokens>
 __device__ __forceinline__ void cursor_next(Cursor& c, const PartialParams& p, int tpp) {
   ++c.t;
   if (++c.sub == tpp) { c.sub = 0; ++c.pk; }
   if (c.t < c.ntile) return;
-  do cursor_request(c, p, c.b + 1); while (c.ntile == 0 && c.b + 1 < p.part.batch);
+  do cursor_request<T>(c, p, c.b + 1); while (c.ntile == 0 && c.b + 1 < p.part.batch);
   c.t = c.pk = c.sub = 0;
 }
 

@@ -8,7 +8,7 @@
 namespace dcp {
 
 constexpr int kMlaTile = 32;
-constexpr int kGqaTile = 32;
+constexpr int kGqaTile = 16;
 
 int mla_heads_per_group(int num_q_heads);
 int gqa_kv_heads_per_group(int num_kv_heads);

@@ -9,21 +9,24 @@
 // Design for gfx950:
 //  * One wave per KV head, up to 4 KV heads per work-group, so a token's K slice and
 //    V slice of the group are contiguous (256 bytes per head).  The work-group owns a
-//    token-balanced span of the rank's 32-token tiles (same partitioning as the MLA
-//    kernel).
-//  * Tiles (K part + V part, 2 x 32 rows x 256 B per head) stream HBM -> LDS through
-//    a two-stage ring of 16-byte direct-to-LDS copies: the next tile is in flight
-//    while this one is computed.  A 32-token tile starts at a multiple of 32 and page
-//    boundaries fall at multiples of the block size (a multiple of 16), so each
-//    16-row half of a tile lies in one page: a copy's source is a per-tile scalar
-//    page base plus a precomputed 32-bit lane offset, with no per-token arithmetic.
+//    span of the rank's 16-token tiles of equal work (same partitioning as the MLA
+//    kernels).
+//  * The loop does little arithmetic per byte (16 query heads per KV head), so what
+//    sets its speed is how many bytes are in flight while memory latency runs under
+//    a full HBM stream.  Tiles are 16 tokens (K part + V part, 2 x 16 rows x 256 B per
+//    head: 32 KB for 4 KV heads) in a 4-stage ring of 16-byte direct-to-LDS copies,
+//    so three tiles are in flight while one is computed.  A 16-token tile never
+//    crosses a page (page sizes are multiples of 16), so a copy's source is one
+//    scalar page base per tile plus a 32-bit lane offset computed once.
 //  * Rows are XOR-swizzled inside each head's 16 chunks (x(r) = 2 (r & 7)): with the
 //    gfx950 pass grouping of ds_read_b128 (lane quads of even / odd popcount within
 //    each half-wave) the K operand reads hit 16 distinct bank groups per pass, and
 //    the transposing V read stays at two lanes per bank.
-//  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the group's
-//    (up to 16) query heads on the columns, V^T through ds_read_b64_tr_b16; base-2
-//    online softmax with the same lazy rescale as the MLA kernel.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (the 16 tokens on the rows, the KV
+//    head's query heads on the columns); O^T += V^T P^T on v_mfma_f32_16x16x16_bf16,
+//    whose A operand (16 dims x 4 tokens per lane quad) is exactly what one
+//    ds_read_b64_tr_b16 returns and whose B operand is the S^T layout; base-2 online
+//    softmax with the same lazy rescale as the MLA kernels.
 //  * Rows of a request's partial last tile past its end are copied from the page
 //    (always inside the pool) and made inert: scores -inf, V part zeroed in LDS.
 //    Finished pieces are stored after the next barrier, ahead of the next copies.
@@ -35,8 +38,8 @@ namespace gqa {
 
 constexpr int kD = 128;
 constexpr int kHeadBytes = kD * 2;  // 256
-constexpr int kTile = kTileTokens;  // 32
-constexpr int kStages = 2;
+constexpr int kTile = 16;           // tokens per tile
+constexpr int kRingBytes = 128 * 1024;
 constexpr float kRescaleSlack = 8.0f;
 static_assert(kGqaTile == kTile, "tile size");
 
@@ -47,19 +50,26 @@ struct Cfg {
   static constexpr int kChunks = kRowBytes / 16;            // 16 * KVW
   static constexpr int kHalfBytes = kTile * kRowBytes;      // K (or V) part of a stage
   static constexpr int kStageBytes = 2 * kHalfBytes;
-  static constexpr int kCopies = kTile * kChunks / kThreads;  // 8 per wave for K, 8 for V
-  static constexpr int kRowsPerCopy = 64 / kChunks;         // rows one wave-wide copy covers
-  static_assert(kCopies == 8 && 16 % kRowsPerCopy == 0, "copy geometry");
+  static constexpr int kStages = kRingBytes / kStageBytes > 4 ? 4 : kRingBytes / kStageBytes;
+  static constexpr int kCopies = kTile * kChunks / kThreads;  // per wave: 4 for K, 4 for V
+  static constexpr int kTileOps = 2 * kCopies;                // copy instructions per wave and tile
+  static_assert(kCopies == 4, "copy geometry");
+  static_assert(kStages >= 3 && (kStages - 2) * kTileOps < 64, "ring depth");
 };
 
 // Chunk c (0 .. 16*KVW-1) of tile row r sits at position c ^ x(r) of the row; the
 // XOR stays inside the head's 16 chunks.
 __device__ __forceinline__ constexpr int row_swz(int r) { return 2 * (r & 7); }
 
+__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                   __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
 template <int KVW>
 __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams p) {
   using C = Cfg<KVW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   __shared__ int64_t s_scan[C::kThreads];
   __shared__ int64_t s_loc[4];
 
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   if (loc.start >= loc.end) return;
   const int total = (int)(loc.end - loc.start);
   const int bs = p.block_size;
-  const int tpp = bs >= kTile ? bs / kTile : 1;  // whole tiles per page (bs >= 32), else 1
+  const int tpp = bs / kTile;  // tiles per page
 
   const int H = p.num_q_heads;
   const int Hkv = p.num_kv_heads;
@@ -88,27 +98,24 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   const bool head_ok = l16 < G;
   const int head = g * G + (head_ok ? l16 : 0);  // this lane's query head (S^T column)
   const int64_t row_stride = (int64_t)Hkv * kHeadBytes;  // bytes between token rows in the pool
+  const int64_t page_bytes = (int64_t)bs * row_stride;
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
   // This lane's copies: LDS slot s = (k * KVW + wave) * 64 + lane of a tile half is
-  // position s % kChunks of row s / kChunks, which holds chunk (pos ^ x(row)).  The
-  // source offset is relative to the row's 16-row half; copy k of this wave covers
-  // rows of one half only (hi_copy: the second).
+  // position s % kChunks of row s / kChunks, which holds chunk (pos ^ x(row)).
   uint32_t ld_off[C::kCopies];
-  bool hi_copy[C::kCopies];
 #pragma unroll
   for (int k = 0; k < C::kCopies; ++k) {
     const int s = (k * KVW + wave) * 64 + lane;
     const int row = s / C::kChunks;
     const int pos = s - row * C::kChunks;
-    ld_off[k] = (uint32_t)((row & 15) * row_stride + g0 * kHeadBytes + (pos ^ row_swz(row)) * 16);
-    hi_copy[k] = ((k * KVW + wave) * C::kRowsPerCopy) >= 16;
+    ld_off[k] = (uint32_t)(row * row_stride + g0 * kHeadBytes + (pos ^ row_swz(row)) * 16);
   }
 
-  // Operand offsets inside a stage half.  K: token block mt, row 16 mt + l16, chunk
-  // 16 wave + 4 s + q4 -> ka[s] (+16 rows for mt = 1).  V: row 4 q4 + l16/4 (+16),
-  // dims 16 m + 4 (l16 % 4) .. +3 = chunk 16 wave + 2 m + (l16 % 4) / 2, byte half
-  // l16 % 2 -> va[m].
+  // Operand offsets inside a stage half.  K: row l16, chunk 16 wave + 4 s + q4 of
+  // k-step s -> ka[s].  V^T of dim block m: row 4 q4 + l16 / 4, dims 16 m + 4 (l16 % 4)
+  // .. +3, i.e. chunk 16 wave + 2 m + (l16 % 4) / 2, byte half l16 % 2 -> va[m]; the
+  // transposing read then gives lane (q4, l16) dim 16 m + l16 of tokens 4 q4 .. +3.
   uint32_t ka[4], va[8];
   {
     const int r = l16;
@@ -127,28 +134,21 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   }
 
   Cursor lc, cc;
-  cursor_set(lc, p, tpp, loc.b0, (int)loc.off0);
+  cursor_set<kTile>(lc, p, tpp, loc.b0, (int)loc.off0);
   cc = lc;
 
-  // Copy source of the loader's tile: the pool byte offsets of its two 16-row halves.
-  // Past the end of the span the loader stays on the last tile, which is copied again
+  // Copy source of the loader's tile (the pool byte offset of its first row).  Past
+  // the end of the span the loader stays on the last tile, which is copied again
   // into a stage no wave reads.
   int lc_left = total;
-  int64_t src_lo = 0, src_hi = 0;
+  int64_t src = 0;
   auto next_src = [&]() {
-    const int64_t tok0 = (int64_t)lc.t * kTile;
-    const int64_t t1 = tok0 + 16;
-    const int32_t pg0 = clamp_page(ld_const(lc.bt_row + tok0 / bs), p.num_cache_blocks);
-    // A second half with no valid row may lie past the request's last page (and past
-    // its block-table row): it then reuses the first half's page, in bounds.
-    const int32_t pg1 = lc.Lr - tok0 > 16 ? clamp_page(ld_const(lc.bt_row + t1 / bs), p.num_cache_blocks)
-                                          : pg0;
-    src_lo = ((int64_t)pg0 * bs + tok0 % bs) * row_stride;
-    src_hi = ((int64_t)pg1 * bs + t1 % bs) * row_stride;
+    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    src = uniform64(page * page_bytes + (int64_t)lc.sub * kTile * row_stride);
   };
   auto advance_loader = [&]() {
     if (--lc_left > 0) {
-      cursor_next(lc, p, tpp);
+      cursor_next<kTile>(lc, p, tpp);
       next_src();
     }
   };
@@ -157,20 +157,27 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     DCP_LDS uint8_t* vdst = kdst + C::kHalfBytes;
 #pragma unroll
     for (int k = 0; k < C::kCopies; ++k) {
-      const int64_t base = hi_copy[k] ? src_hi : src_lo;
-      copy16(p.k_cache + base, ld_off[k], lds_addr(kdst + (k * KVW + wave) * 1024));
-      copy16(p.v_cache + base, ld_off[k], lds_addr(vdst + (k * KVW + wave) * 1024));
+      copy16(p.k_cache + src, ld_off[k], lds_addr(kdst + (k * KVW + wave) * 1024));
+      copy16(p.v_cache + src, ld_off[k], lds_addr(vdst + (k * KVW + wave) * 1024));
     }
   };
 
   // q[b, head, 32 s + 8 q4 .. +7]: the B operand of S^T = K Q^T for k-step s.  Lanes
   // of heads past the group load the group's first head: their columns are
-  // independent of the others and never stored.
-  bf16x8 qreg[4];
-  auto load_q = [&](int b) {
+  // independent of the others and never stored.  The loads are asm, so the
+  // compiler's wait counting (which cannot see the copies either) does not drain
+  // the ring before every use; the next request's slice goes to qnext ahead of a
+  // copy round, and the loop's own wait covers it before it moves into qreg.
+  bf16x8 qreg[4], qnext[4];
+  auto load_q = [&](bf16x8 (&dst)[4], int b) {
     const uint16_t* qp = p.q + ((int64_t)b * H + head) * kD + 8 * q4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qreg[s] = *(const bf16x8*)(qp + 32 * s);
+    for (int s = 0; s < 4; ++s)
+      asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[s]) : "v"(qp), "n"(64 * s) : "memory");
+  };
+  auto settle = [&](bf16x8 (&r)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(r[s]));
   };
 
   f32x4 oacc[8];
@@ -197,35 +204,55 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     }
   };
 
-  // Zero the V rows nvalid..31 of the tile at `vb` (the V half of a stage).
+  // Zero the V rows nvalid..15 of the tile at `vb` (the V half of a stage).
   auto zero_tail = [&](DCP_LDS uint8_t* vb, int nvalid) {
     const int n = (kTile - nvalid) * C::kChunks;
     for (int e = tid; e < n; e += C::kThreads)
       zero_lds16(lds_addr(vb + nvalid * C::kRowBytes + e * 16));
   };
 
-  // ---- prologue: query slice and the first tile
-  load_q(cc.b);
+  // ---- prologue: query slice and the first kStages-1 tiles
+  load_q(qreg, cc.b);
   next_src();
-  issue(0);
-  advance_loader();
+#pragma unroll
+  for (int t = 0; t < C::kStages - 1; ++t) {
+    issue(t);
+    advance_loader();
+  }
   int piece_t0 = cc.t;
   bool first_piece = true;
+  bool q_moved = true;  // the slice for tile 0 was loaded before the prologue's copies
 
   for (int i = 0; i < total; ++i) {
-    // Tile i (issued last iteration) and any query load have landed: this wave has
-    // nothing else outstanding but piece stores, which only make the wait stricter.
-    // The barrier then also guarantees every wave has finished tile i-1, whose stage
-    // the copies below refill.
-    wait_vmcnt_builtin<0>();
+    // Tile i has landed once only the copies of the kStages-2 younger tiles are
+    // outstanding; after a query load (issued just before the previous copy round)
+    // only that round may be, which also completes the load.  Piece stores sit
+    // between copy rounds and only make the wait stricter.  The barrier then also
+    // guarantees every wave has finished tile i-1, whose stage the copies below refill.
+    if (q_moved) wait_vmcnt_builtin<C::kTileOps * (C::kStages - 2) - C::kTileOps * (C::kStages - 3)>();
+    else wait_vmcnt_builtin<(C::kStages - 2) * C::kTileOps>();
+    if (q_moved && i > 0) {
+      settle(qnext);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qreg[s] = qnext[s];
+    }
+    settle(qreg);
+    q_moved = false;
     wg_barrier();
     wait_lgkm();
     flush_piece();
-    issue((i + 1) & 1);
-
-    DCP_LDS uint8_t* kb = lds + (i & 1) * C::kStageBytes;
-    DCP_LDS uint8_t* vb = kb + C::kHalfBytes;
     const Cursor cur = cc;
+    if (i + 1 < total) {
+      cursor_next<kTile>(cc, p, tpp);
+      if (cc.b != cur.b) {  // tile i+1 starts the next request: fetch its slice now
+        load_q(qnext, cc.b);
+        q_moved = true;
+      }
+    }
+    issue((i + C::kStages - 1) % C::kStages);
+
+    DCP_LDS uint8_t* kb = lds + (i % C::kStages) * C::kStageBytes;
+    DCP_LDS uint8_t* vb = kb + C::kHalfBytes;
     const int nvalid = cur.Lr - cur.t * kTile;  // >= kTile for every tile but a request's last
     if (nvalid < kTile) {
       zero_tail(vb, nvalid);
@@ -233,36 +260,23 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       wg_barrier();
     }
 
-    // ---- S^T [32 tokens x 16 heads] as two 16x16 tiles
-    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    // ---- S^T [16 tokens x 16 heads]
+    f32x4 sacc = f32x4{};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 a0 = *(const DCP_LDS bf16x8*)(kb + ka[s]);
-      const bf16x8 a1 = *(const DCP_LDS bf16x8*)(kb + ka[s] + 16 * C::kRowBytes);
-      sacc[0] = mfma16x16x32(a0, qreg[s], sacc[0]);
-      sacc[1] = mfma16x16x32(a1, qreg[s], sacc[1]);
-    }
-    if (i + 1 < total) {
-      cursor_next(cc, p, tpp);
-      if (cc.b != cur.b) load_q(cc.b);
-    }
+    for (int s = 0; s < 4; ++s) sacc = mfma16x16x32(*(const DCP_LDS bf16x8*)(kb + ka[s]), qreg[s], sacc);
 
-    // ---- online softmax (base 2); lane: head l16, tokens 16 (j / 4) + 4 q4 + j % 4
-    float x[8];
+    // ---- online softmax (base 2); lane: head l16, tokens 4 q4 + j
+    float x[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int tok = 16 * (j >> 2) + 4 * q4 + (j & 3);
-      x[j] = tok < nvalid ? sacc[j >> 2][j & 3] * p.scale_log2 : -INFINITY;
-    }
-    float mloc = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    for (int j = 0; j < 4; ++j) x[j] = 4 * q4 + j < nvalid ? sacc[j] * p.scale_log2 : -INFINITY;
+    float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mloc = max_over_groups(mloc);
     const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
     const float alpha = fast_exp2(m_run - m_new);
     float lsum = 0.f;
-    bf16x8 pb;
+    bf16x4 pb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const float pr = fast_exp2(x[j] - m_new);
       lsum += pr;
       pb[j] = (__bf16)pr;
@@ -275,13 +289,10 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     }
     m_run = m_new;
 
-    // ---- O^T [128 dims x 16 heads] += V^T [128 x 32 tokens] P^T [32 x 16]
+    // ---- O^T [128 dims x 16 heads] += V^T [128 x 16 tokens] P^T [16 x 16]
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const u32x2 v1 = lds_read_tr16(vb + va[m]);
-      const u32x2 v2 = lds_read_tr16(vb + va[m] + 16 * C::kRowBytes);
-      oacc[m] = mfma16x16x32(join_tr16(v1, v2), pb, oacc[m]);
-    }
+    for (int m = 0; m < 8; ++m)
+      oacc[m] = mfma16x16x16(__builtin_bit_cast(bf16x4, lds_read_tr16(vb + va[m])), pb, oacc[m]);
 
     // ---- end of a request piece: normalisation and destination; stored after the
     // next barrier
