@@ -147,7 +147,7 @@ struct SpanLoc {
 // Block-cooperative: every thread of the block gets the location of span w.  If
 // prefix_out is non-null, the block also writes each request's first tile index
 // (prefix_out[b], the total at prefix_out[B]) and weighted position (prefix_out[B +
-// 1 + b], the weighted total at prefix_out[2 B + 1]).  s_scan must hold blockDim.x
+// 1 + b], the weighted total at prefix_out[2 B + 1]).  s_scan must hold blockDim.x / 64
 // int64 values; s_loc four int64 values.
 template <int NT>
 __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
@@ -162,19 +162,27 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
     const int64_t n = part_tiles(a, b);
     sum += (n << kCountBits) | (n > 0 ? 1 : 0);
   }
-  s_scan[tid] = sum;
+  // Inclusive scan of the per-thread sums: within each wave by shuffles, then the
+  // wave totals through LDS (one barrier instead of two per doubling step).
+  static_assert(NT % 64 == 0 && NT / 64 <= 16, "block shape");
+  const int lane = tid & 63;
+  int64_t incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t u = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) s_scan[tid >> 6] = incl;
   if (tid == 0) { s_loc[0] = -1; s_loc[1] = 0; s_loc[2] = 0; s_loc[3] = 0; }
   __syncthreads();
-  // Hillis-Steele inclusive scan over the per-thread sums.
-  for (int d = 1; d < NT; d <<= 1) {
-    int64_t v = tid >= d ? s_scan[tid - d] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
+  int64_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const int64_t wt = s_scan[k];
+    if (k < (tid >> 6)) incl += wt;
+    tot += wt;
   }
-  const int64_t incl = s_scan[tid];
   const int64_t excl = incl - sum;
-  const int64_t tot = s_scan[NT - 1];
   const int64_t A = a.req_weight;
   const int64_t TT = tot >> kCountBits;
   const int64_t WT = TT + A * (tot & kCountMask);
