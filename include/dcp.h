@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
   DCP_SUCCESS = 0,
   DCP_ERROR_INVALID_VALUE = 1, /* a null pointer, a size or an index out of range */
-  DCP_ERROR_NOT_SUPPORTED = 2, /* a valid shape this build has no kernel for */
+  DCP_ERROR_NOT_SUPPORTED = 2, /* a valid shape the library has no kernel for */
   DCP_ERROR_WORKSPACE = 3,     /* workspace missing or smaller than required */
   DCP_ERROR_HIP = 4            /* the HIP runtime reported an error */
 } dcp_status_t;
