@@ -17,6 +17,13 @@ With --bands it instead prints one JSON line with rank 0's partial-call bandwidt
 each request-length band of the pages' comparison by sequence length (<32k, 32-64k,
 64-128k, 128-200k, >=200k tokens): the long-context MLA shape with requests drawn from
 the synthetic mix restricted to the band, as many as give rank 0 about 1.25M tokens.
+
+With --next it instead prints one JSON line timing the steps next to the hot path on the
+long-context MLA batch: rank 0's partial for 2 and 4 query tokens per request (multi-token
+decode queries, causal by global position), the append of every request's newest latent
+row into its owner rank's page (all N ranks' calls), and the merge as per-rank steps
+(global LSE from the gathered LSEs, local rescale with fp32 or bf16 transport, one rank's
+head slice of the sum) beside the fused N-way merge.
 """
 from __future__ import annotations
 
@@ -51,6 +58,9 @@ def parse():
                     help="seconds of oracle math to time for the CPU baseline")
     ap.add_argument("--bands", action="store_true",
                     help="rank-0 partial bandwidth per request-length band instead of the step")
+    ap.add_argument("--next", action="store_true",
+                    help="time the steps next to the hot path (multi-token queries, KV append, "
+                         "per-rank merge steps) instead of the step")
     ap.add_argument("--copy-probe-bytes", type=int, default=0,
                     help="before timing, run one plain device-to-device copy of this many bytes "
                          "(a reference for scaling the HBM byte counters of a profiler run)")
@@ -188,6 +198,110 @@ def run_bands(args):
     }), flush=True)
 
 
+def _event_ms(fn, steps: int, warmup: int) -> float:
+    """Mean milliseconds of fn() over `steps` calls, HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def run_next(args):
+    """Multi-token queries, KV append and the per-rank merge steps on the long-context
+    MLA batch (the workload of --workload, default B=128, 64 heads, N=8, I=128)."""
+    import torch
+    import dcp_inputs as di
+    import decode_attention_sequence_paged_amd as dcp
+    from dcp_inputs import paged
+
+    dcp.lib()
+    torch.cuda.set_device(0)
+    wl = di.WORKLOADS[args.workload]
+    if wl.kind != "mla":
+        raise SystemExit("--next runs on an MLA workload")
+    N, B, H, Dqk, Dv, bs = wl.dcp_size, wl.batch, wl.num_q_heads, wl.qk_dim, wl.v_dim, wl.block_size
+    desc = paged.desc_for(wl)
+    sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+    out = {"metric": "steps next to the hot path: multi-token partial, KV append, per-rank merge steps",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": describe(wl)}}
+
+    # multi-token decode queries: rank 0's call for q_len = 1, 2, 4
+    rc = paged.build_rank_cache(wl, 0)
+    pages = int(((rc.local_lens + bs - 1) // bs).sum())
+    kv = rc.total_local * Dqk * 2
+    mtp = []
+    for q_len in (1, 2, 4):
+        qw = di.Workload(**dict(wl.__dict__, batch=B * q_len, lengths=tuple(wl.lengths) * q_len))
+        q = paged.device_query(qw).view(B, q_len, H, Dqk)
+        ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(desc, q_len, B, 0), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty((B, q_len, H, Dv), device="cuda")
+        lse = torch.empty((B, q_len, H), device="cuda")
+        t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl,
+                                                          0, N, wl.interleave, ws, o, lse),
+                      args.steps, args.warmup)
+        call = kv + B * q_len * H * (Dqk * 2 + Dv * 4 + 4) + pages * 4
+        mtp.append({"q_len": q_len, "score_rows_per_request": q_len * H, "rank0_call_ms": round(t, 4),
+                    "rank0_kv_gbps": round(kv / (t * 1e-3) / 1e9, 1),
+                    "roofline_frac": round(call / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "flops_per_s": round(2.0 * q_len * H * (Dqk + Dv) * rc.total_local / (t * 1e-3), 1)})
+        del q, ws, o, lse
+    out["multi_token_queries"] = mtp
+    del rc
+    torch.cuda.empty_cache()
+
+    # KV append: every rank's call; only the owner of position L-1 writes a request's row
+    caches = [paged.build_rank_cache(wl, r) for r in range(N)]
+    new_k = torch.randn((B, Dqk), device="cuda").to(torch.bfloat16)
+
+    def append_all():
+        for r in range(N):
+            dcp.dcp_append_kv(desc, new_k, None, caches[r].k_cache, None, caches[r].block_table, sl,
+                              r, N, wl.interleave)
+    t = _event_ms(append_all, args.steps, args.warmup)
+    out["kv_append"] = {"calls": N, "step_ms": round(t, 4), "call_us": round(1e3 * t / N, 2),
+                        "rows_written": B, "bytes_written": B * Dqk * 2}
+    del caches
+    torch.cuda.empty_cache()
+
+    # the merge as per-rank steps, on partials of the real shape
+    o_all = torch.randn((N, B, H, Dv), device="cuda")
+    l_all = torch.randn((N, B, H), device="cuda") + 10.0
+    o = torch.empty((B, H, Dv), device="cuda")
+    lse = torch.empty((B, H), device="cuda")
+    gl = torch.empty((B, H), device="cuda")
+    row = B * H * Dv * 4
+    t_fused = _event_ms(lambda: dcp.dcp_merge(o_all, l_all, o, lse), args.steps, args.warmup)
+    t_lse = _event_ms(lambda: dcp.dcp_merge_lse(l_all, gl), args.steps, args.warmup)
+    steps = {"fused_merge_ms": round(t_fused, 4),
+             "fused_merge_gbps": round((N + 1) * B * H * (Dv + 1) * 4 / (t_fused * 1e-3) / 1e9, 1),
+             "merge_lse_ms": round(t_lse, 4)}
+    for name, dt, esz in (("fp32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+        scaled = torch.empty((N, B, H, Dv), dtype=dt, device="cuda")
+        sl_out = torch.empty((B, H // N, Dv), device="cuda")
+        t_res = _event_ms(lambda: dcp.dcp_rescale_partial(o_all[0], l_all[0], gl, scaled[0]),
+                          args.steps, args.warmup)
+        t_sum = _event_ms(lambda: dcp.dcp_sum_head_slice(scaled, 0, sl_out), args.steps, args.warmup)
+        steps["rescale_%s_ms" % name] = round(t_res, 4)
+        steps["rescale_%s_gbps" % name] = round((row + B * H * 8 + B * H * Dv * esz) / (t_res * 1e-3) / 1e9, 1)
+        steps["sum_head_slice_%s_ms" % name] = round(t_sum, 4)
+        steps["sum_head_slice_%s_gbps" % name] = round(
+            (N * B * (H // N) * Dv * esz + B * (H // N) * Dv * 4) / (t_sum * 1e-3) / 1e9, 1)
+        steps["per_rank_%s_ms" % name] = round(t_lse + t_res + t_sum, 4)
+        del scaled, sl_out
+    out["merge_steps"] = steps
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -198,6 +312,9 @@ def main():
 
     if args.bands:
         run_bands(args)
+        return
+    if args.next:
+        run_next(args)
         return
 
     import torch

@@ -152,7 +152,7 @@ def test_merge_kernel_against_oracle():
 
 # ----------------------------------------------------------------------------- configurations
 
-@pytest.mark.parametrize("parts", [0, 1, 5, 64])
+@pytest.mark.parametrize("parts", [0, 1, 5, 16, 64])
 def test_mla_tiny_every_rank_and_merge(parts):
     """B=2, 16 heads, seq_lens {1000, 3000}, block size 64, N=2, I=1."""
     wl = di.WORKLOADS["mla_tiny"]
