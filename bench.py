@@ -20,7 +20,7 @@ the synthetic mix restricted to the band, as many as give rank 0 about 1.25M tok
 
 With --next it instead prints one JSON line timing the steps next to the hot path on the
 long-context MLA batch: rank 0's partial for 2 and 4 query tokens per request (multi-token
-decode queries, causal by global position), the append of every request's newest latent
+decode queries, causal by global position; also on the GQA batch), the append of every request's newest latent
 row into its owner rank's page (all N ranks' calls), and the merge as per-rank steps
 (global LSE from the gathered LSEs, local rescale with fp32 or bf16 transport, one rank's
 head slice of the sum) beside the fused N-way merge.
@@ -257,6 +257,33 @@ def run_next(args):
         del q, ws, o, lse
     out["multi_token_queries"] = mtp
     del rc
+    torch.cuda.empty_cache()
+
+    # GQA multi-token queries (one single-token pass per query token): rank 0 of the GQA batch
+    gw = di.WORKLOADS["gqa_b32"]
+    gdesc = paged.desc_for(gw)
+    gsl = torch.tensor(np.asarray(gw.lengths, dtype=np.int32), device="cuda")
+    grc = paged.build_rank_cache(gw, 0)
+    GB, GH = gw.batch, gw.num_q_heads
+    gkv = grc.total_local * gw.num_kv_heads * (gw.qk_dim + gw.v_dim) * 2
+    gmtp = []
+    for q_len in (1, 2, 4):
+        qw = di.Workload(**dict(gw.__dict__, batch=GB * q_len, lengths=tuple(gw.lengths) * q_len))
+        q = paged.device_query(qw).view(GB, q_len, GH, gw.qk_dim)
+        ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(gdesc, q_len, GB, 0), dtype=torch.uint8,
+                         device="cuda")
+        o = torch.empty((GB, q_len, GH, gw.v_dim), device="cuda")
+        lse = torch.empty((GB, q_len, GH), device="cuda")
+        t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(gdesc, q, grc.k_cache, grc.v_cache,
+                                                          grc.block_table, gsl, 0, gw.dcp_size,
+                                                          gw.interleave, ws, o, lse),
+                      args.steps, args.warmup)
+        gmtp.append({"q_len": q_len, "passes": q_len, "rank0_call_ms": round(t, 4),
+                     "rank0_kv_gbps_per_query_token": round(gkv * q_len / (t * 1e-3) / 1e9, 1),
+                     "ms_per_query_token": round(t / q_len, 4)})
+        del q, ws, o, lse
+    out["gqa_multi_token_queries"] = {"workload": describe(gw), "rows": gmtp}
+    del grc
     torch.cuda.empty_cache()
 
     # KV append: every rank's call; only the owner of position L-1 writes a request's row

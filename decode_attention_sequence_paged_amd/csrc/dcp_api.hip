@@ -17,6 +17,7 @@ constexpr int32_t kMaxBatch = 1 << 16;
 constexpr int32_t kMaxParts = 1 << 16;
 constexpr int32_t kMaxMlaRows = 512;  // MLA score rows (query tokens x heads) per request
 constexpr int64_t kMaxMtpRows = kMaxMlaRows;
+constexpr int32_t kMaxGqaQueryTokens = 64;  // query tokens per request of a GQA multi-token call
 constexpr int32_t kMaxDevices = 64;
 
 // Read-only cache of the compute-unit count per device (filled on first use).
@@ -90,13 +91,16 @@ WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   return l;
 }
 
-// Multi-token decode queries: q_len query tokens of num_q_heads heads become
-// q_len * num_q_heads score rows (MLA only).
+// Multi-token decode queries.  MLA: q_len query tokens of num_q_heads heads become
+// q_len * num_q_heads score rows of one pass.  GQA: one pass per query token (the
+// kernel keeps a KV head's query heads on the 16 MFMA columns), so the shapes are
+// those of a single-token call.
 dcp_status_t check_q_len(const dcp_attn_desc_t* d, int32_t q_len, dcp_attn_desc_t* rows) {
   *rows = *d;
   if (q_len < 1) return DCP_ERROR_INVALID_VALUE;
   if (q_len == 1) return DCP_SUCCESS;
-  if (d->kind != DCP_KV_MLA_LATENT) return DCP_ERROR_NOT_SUPPORTED;
+  if (d->kind == DCP_KV_GQA) return q_len <= kMaxGqaQueryTokens ? DCP_SUCCESS : DCP_ERROR_NOT_SUPPORTED;
+  if (d->kind != DCP_KV_MLA_LATENT) return DCP_ERROR_INVALID_VALUE;
   if (d->num_q_heads < 1 || (int64_t)q_len * d->num_q_heads > kMaxMtpRows) return DCP_ERROR_NOT_SUPPORTED;
   rows->num_q_heads = q_len * d->num_q_heads;
   return DCP_SUCCESS;
@@ -269,16 +273,14 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   p.part.tile = d.kind == DCP_KV_MLA_LATENT ? dcp::kMlaTile : dcp::kGqaTile;
   p.part.num_parts = parts;
   p.part.req_weight = request_weight(&d);
+  p.part.len_offset = 0;
   p.out_o = out_o;
   p.out_lse = out_lse;
+  p.q_req_stride = (int64_t)d.num_q_heads * d.qk_dim;
+  p.out_req_rows = d.num_q_heads;
   p.ws_prefix = (int64_t*)(ws + wl.prefix);
   p.ws_lse = (float*)(ws + wl.lse);
   p.ws_o = (float*)(ws + wl.o);
-
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = d.kind == DCP_KV_MLA_LATENT ? dcp::launch_mla_partial(p, s)
-                                             : dcp::launch_gqa_partial(p, s);
-  if (e != hipSuccess) return DCP_ERROR_HIP;
 
   dcp::SplitReduceParams r{};
   r.ws_prefix = p.ws_prefix;
@@ -289,9 +291,34 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   r.v_dim = d.v_dim;
   r.num_parts = parts;
   r.req_weight = p.part.req_weight;
+  r.out_req_rows = d.num_q_heads;
   r.out_o = out_o;
   r.out_lse = out_lse;
-  return hip_status(dcp::launch_split_reduce(r, s));
+
+  hipStream_t s = (hipStream_t)stream;
+  if (d.kind == DCP_KV_MLA_LATENT) {
+    if (dcp::launch_mla_partial(p, s) != hipSuccess) return DCP_ERROR_HIP;
+    return hip_status(dcp::launch_split_reduce(r, s));
+  }
+  // GQA: query token i of a request at global length L sees the positions <= L - q_len
+  // + i, i.e. the single-token problem at length L - (q_len - 1 - i).  One pass per
+  // query token, each over its own slices of q [B, q_len, H, D] and of the outputs
+  // [B, q_len, H, .]; the passes reuse the workspace in stream order.
+  p.q_len = 1;
+  for (int32_t i = 0; i < q_len; ++i) {
+    p.part.len_offset = q_len - 1 - i;
+    p.q = (const uint16_t*)q + (int64_t)i * d.num_q_heads * d.qk_dim;
+    p.q_req_stride = (int64_t)q_len * d.num_q_heads * d.qk_dim;
+    p.out_o = out_o + (int64_t)i * d.num_q_heads * d.v_dim;
+    p.out_lse = out_lse + (int64_t)i * d.num_q_heads;
+    p.out_req_rows = (int64_t)q_len * d.num_q_heads;
+    r.out_o = p.out_o;
+    r.out_lse = p.out_lse;
+    r.out_req_rows = p.out_req_rows;
+    if (dcp::launch_gqa_partial(p, s) != hipSuccess) return DCP_ERROR_HIP;
+    if (dcp::launch_split_reduce(r, s) != hipSuccess) return DCP_ERROR_HIP;
+  }
+  return DCP_SUCCESS;
 }
 
 dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,

@@ -116,7 +116,7 @@ __device__ __forceinline__ T ld_const(const T* ptr) {
 
 // Local length of request b actually processed (clamped to what its block table row holds).
 __device__ __forceinline__ int64_t part_local_len(const PartitionArgs& a, int b) {
-  int64_t L = ld_const(a.seq_lens + b);
+  int64_t L = (int64_t)ld_const(a.seq_lens + b) - a.len_offset;
   int64_t lr = dcp_local_len(L < 0 ? 0 : L, a.num_ranks, a.interleave, a.rank);
   const int64_t cap = (int64_t)a.max_blocks_per_seq * a.block_size;
   return lr < cap ? lr : cap;
@@ -259,7 +259,7 @@ struct Cursor {
 template <int T = kTileTokens>
 __device__ __forceinline__ void cursor_request(Cursor& c, const PartialParams& p, int b) {
   c.b = b;
-  const int32_t L = ld_const(p.part.seq_lens + b);
+  const int32_t L = ld_const(p.part.seq_lens + b) - p.part.len_offset;
   c.Lg = L < 0 ? 0 : L;
   c.Lr = (int)part_local_len(p.part, b);
   c.ntile = (c.Lr + T - 1) / T;

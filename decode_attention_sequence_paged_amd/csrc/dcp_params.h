@@ -14,6 +14,7 @@ struct PartitionArgs {
   int32_t tile;             // tokens per tile
   int32_t num_parts;        // P
   int32_t req_weight;       // tiles of work charged to each request with local tokens
+  int32_t len_offset;       // subtracted from every seq_lens entry (a query token's causal length)
 };
 
 struct PartialParams {
@@ -31,6 +32,9 @@ struct PartialParams {
   PartitionArgs part;
   float* out_o;             // [B, H, v_dim]
   float* out_lse;           // [B, H]
+  int64_t q_req_stride;     // GQA: query elements between consecutive requests (H * qk_dim unless a
+                            // query token of a multi-token batch)
+  int64_t out_req_rows;     // GQA: output rows between consecutive requests (H unless likewise)
   int64_t* ws_prefix;       // [2 (B + 1)]: tile prefix, then weighted prefix
   float* ws_lse;            // [2P, H]
   float* ws_o;              // [2P, H, v_dim]
@@ -42,6 +46,8 @@ struct SplitReduceParams {
   const float* ws_lse;       // [2P, H]
   const float* ws_o;         // [2P, H, v_dim]
   int32_t batch, num_heads, v_dim, num_parts, req_weight;
+  int64_t out_req_rows;      // output rows between consecutive requests (num_heads, or q_len *
+                             // num_heads for one query token of a multi-token GQA batch)
   float* out_o;              // [B, H, v_dim]
   float* out_lse;            // [B, H]
 };

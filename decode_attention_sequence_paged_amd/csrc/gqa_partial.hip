@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   // copy round, and the loop's own wait covers it before it moves into qreg.
   bf16x8 qreg[4], qnext[4];
   auto load_q = [&](bf16x8 (&dst)[4], int b) {
-    const uint16_t* qp = p.q + ((int64_t)b * H + head) * kD + 8 * q4;
+    const uint16_t* qp = p.q + (int64_t)b * p.q_req_stride + (int64_t)head * kD + 8 * q4;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[s]) : "v"(qp), "n"(64 * s) : "memory");
@@ -303,8 +303,8 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       pend = true;
       pend_inv = 1.0f / l_run;
       pend_lse = (m_run + fast_log2(l_run)) * kLn2;
-      pend_o = (whole ? p.out_o + ((int64_t)cur.b * H + head) * kD : p.ws_o + (slot * H + head) * kD) + 4 * q4;
-      pend_l = whole ? p.out_lse + (int64_t)cur.b * H + head : p.ws_lse + slot * H + head;
+      pend_o = (whole ? p.out_o + ((int64_t)cur.b * p.out_req_rows + head) * kD : p.ws_o + (slot * H + head) * kD) + 4 * q4;
+      pend_l = whole ? p.out_lse + (int64_t)cur.b * p.out_req_rows + head : p.ws_lse + slot * H + head;
       piece_t0 = 0;
       first_piece = false;
       m_run = -INFINITY;

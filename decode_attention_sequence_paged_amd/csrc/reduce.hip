@@ -51,11 +51,11 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
 
   const int64_t F = p.ws_prefix[b];
   const int64_t n = p.ws_prefix[b + 1] - F;
-  float* orow = p.out_o + ((int64_t)b * H + head) * DV + 4 * q;
+  float* orow = p.out_o + ((int64_t)b * p.out_req_rows + head) * DV + 4 * q;
   if (n == 0) {  // no local tokens: the merge's neutral element
     if (head_ok && pl == 0) {
       *(f32x4*)orow = f32x4{};
-      if (q == 0) p.out_lse[(int64_t)b * H + head] = -INFINITY;
+      if (q == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = -INFINITY;
     }
     return;
   }
@@ -129,7 +129,7 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
   if (!head_ok) return;
   // a row no piece saw a token for: the merge's neutral element
   *(f32x4*)orow = wsum > 0.f ? acc * (1.0f / wsum) : f32x4{};
-  if (q == 0) p.out_lse[(int64_t)b * H + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
+  if (q == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int DV, int PL>

@@ -191,9 +191,13 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
  *   out_lse  device fp32 [batch, q_len, H], written
  *   workspace  >= dcp_decode_workspace_size_mtp(desc, q_len, batch, num_partitions)
  * Every other argument as for dcp_decode_partial.
- * Supported: MLA with q_len * H <= 512 (GQA: q_len = 1 only, else NOT_SUPPORTED).
+ * Supported: MLA with q_len * H <= 512, computed in one pass with the q_len * H
+ * (query token, head) pairs as score rows; GQA with q_len <= 64, computed as q_len
+ * single-token passes, query token i over the positions below L - (q_len - 1 - i)
+ * (each pass reads the rank's pages of its length again).
  * Errors: INVALID_VALUE (q_len < 1, and as dcp_decode_partial), NOT_SUPPORTED,
- * WORKSPACE, HIP (nothing runs on error).                                      */
+ * WORKSPACE (nothing runs on these), HIP (a GQA call that fails to launch pass i
+ * leaves passes 0 .. i-1 enqueued).                                            */
 size_t dcp_decode_workspace_size_mtp(const dcp_attn_desc_t* desc, int32_t q_len, int32_t batch,
                                      int32_t num_partitions);
 dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, const void* q,

@@ -179,14 +179,17 @@ def test_mtp_entry_point_validation():
     assert dcp.dcp_decode_workspace_size_mtp(mla, 4, 4, 8) > dcp.dcp_decode_workspace_size(mla, 4, 8)
     assert dcp.dcp_decode_workspace_size_mtp(mla, 0, 4, 8) == 0
     assert dcp.dcp_decode_workspace_size_mtp(mla, 9, 4, 8) == 0      # 9 x 64 rows > 512
-    assert dcp.dcp_decode_workspace_size_mtp(gqa, 2, 4, 8) == 0      # GQA: one query token only
-    assert dcp.dcp_decode_workspace_size_mtp(gqa, 1, 4, 8) > 0
+    # GQA: one single-token pass per query token, so a single-token workspace
+    assert dcp.dcp_decode_workspace_size_mtp(gqa, 2, 4, 8) == dcp.dcp_decode_workspace_size(gqa, 4, 8) > 0
+    assert dcp.dcp_decode_workspace_size_mtp(gqa, 64, 4, 8) == dcp.dcp_decode_workspace_size(gqa, 4, 8)
+    assert dcp.dcp_decode_workspace_size_mtp(gqa, 65, 4, 8) == 0
     fake = 1 << 20
     def call(desc=mla, q_len=2, B=2, rank=0):
         return lib.dcp_decode_partial_mtp(ctypes.byref(desc), q_len, fake, fake, 0, 10, fake, 4, fake, B,
                                           rank, 2, 1, 8, fake * 2, 1 << 30, fake, fake, 0)
     assert call(q_len=0) == dcp.DCP_ERROR_INVALID_VALUE
     assert call(q_len=9) == dcp.DCP_ERROR_NOT_SUPPORTED
-    assert call(desc=gqa) == dcp.DCP_ERROR_NOT_SUPPORTED
+    assert call(desc=gqa) == dcp.DCP_ERROR_INVALID_VALUE           # GQA needs its V pool
+    assert call(desc=gqa, q_len=65) == dcp.DCP_ERROR_NOT_SUPPORTED
     assert call(rank=2) == dcp.DCP_ERROR_INVALID_VALUE
     assert call(B=0) == dcp.DCP_SUCCESS

@@ -502,13 +502,14 @@ def run_rank_mtp(wl, rank, q_len, census=False, parts=0):
     pg = _paged()
     B, H = wl.batch, wl.num_q_heads
     rc = pg.build_rank_cache(wl, rank, census=census, lengths=np.asarray(wl.lengths))
-    q = pg.device_query(_wl(wl.name, batch=B * q_len, seed=wl.seed), census=census).view(B, q_len, H, wl.qk_dim)
+    qw = di.Workload(**dict(wl.__dict__, batch=B * q_len, lengths=tuple(wl.lengths) * q_len))
+    q = pg.device_query(qw, census=census).view(B, q_len, H, wl.qk_dim)
     sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
     desc = pg.desc_for(wl)
     ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(desc, q_len, B, parts), dtype=torch.uint8, device="cuda")
     o = torch.full((B, q_len, H, wl.v_dim), float("nan"), device="cuda")
     lse = torch.full((B, q_len, H), float("nan"), device="cuda")
-    dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl, rank, wl.dcp_size,
+    dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, rc.v_cache, rc.block_table, sl, rank, wl.dcp_size,
                                wl.interleave, ws, o, lse, num_partitions=parts)
     torch.cuda.synchronize()
     return o, lse
@@ -520,6 +521,10 @@ MTP_CASES = [
     ("mla_tiny", 3, dict(dcp_size=4, interleave=2, lengths=(7, 9, 2049, 64))),
     ("mla_long_b128", 2, dict(batch=3, lengths=(5000, 20000, 1030))),
     ("mla_long_b128", 4, dict(batch=2, lengths=(3000, 1025))),
+    # GQA: one single-token pass per query token, each over its causal length
+    ("gqa_b32", 2, dict(lengths=(5000, 1, 2, 33))),
+    ("gqa_b32", 3, dict(dcp_size=2, interleave=3, block_size=32, lengths=(1000, 37, 2, 3, 4))),
+    ("gqa_b32", 4, dict(num_q_heads=32, num_kv_heads=8, dcp_size=3, interleave=16, lengths=(2049, 700))),
 ]
 
 
@@ -552,23 +557,26 @@ def test_mtp_every_rank_and_merge(name, q_len, kw, parts):
         check_close(om[b], lm[b], o_ref, l_ref, "mtp merged b=%d" % b)
 
 
-def test_mtp_single_query_is_the_decode_call():
+@pytest.mark.parametrize("name", ["mla_tiny", "gqa_b32"])
+def test_mtp_single_query_is_the_decode_call(name):
     """q_len = 1 through the multi-token entry point is the single-token call, bit for bit."""
-    wl = _wl("mla_tiny", dcp_size=3, interleave=5)
+    wl = _wl(name, dcp_size=3, interleave=5, lengths=(1000, 3000, 17))
     for r in range(wl.dcp_size):
         o1, l1, _ = run_rank(wl, r)
         o2, l2 = run_rank_mtp(wl, r, 1)
         assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
 
 
-@pytest.mark.parametrize("q_len,kw", [(4, dict(dcp_size=3, interleave=5, block_size=32,
-                                                lengths=(1000, 3000, 1, 2, 3, 17))),
-                                      (2, dict(dcp_size=2, interleave=1, lengths=(64, 65)))])
-def test_mtp_census(q_len, kw):
+@pytest.mark.parametrize("name,q_len,kw", [
+    ("mla_tiny", 4, dict(dcp_size=3, interleave=5, block_size=32, lengths=(1000, 3000, 1, 2, 3, 17))),
+    ("mla_tiny", 2, dict(dcp_size=2, interleave=1, lengths=(64, 65))),
+    ("gqa_b32", 3, dict(dcp_size=3, interleave=5, block_size=32, lengths=(1000, 3000, 1, 2, 3, 17))),
+    ("gqa_b32", 2, dict(dcp_size=2, interleave=1, lengths=(16, 17, 33)))])
+def test_mtp_census(name, q_len, kw):
     """q = 0 and V rows = bits of the global token id: for every query, O * count recovers
     exactly how many of the tokens it may see (the rank's tokens at positions
     <= L - q_len + i, enumerated by the oracle) have each bit set."""
-    wl = _wl("mla_tiny", **kw)
+    wl = _wl(name, **kw)
     for r in range(wl.dcp_size):
         o, lse = run_rank_mtp(wl, r, q_len, census=True)
         o, lse = o.cpu().numpy().astype(np.float64), lse.cpu().numpy()
