@@ -43,7 +43,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "local-shard decode-attn KV GB/s & % of HBM peak; decode steps/s per batch"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_partial_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_traffic.json")
 
 
 def parse():
@@ -78,25 +78,29 @@ def describe(wl) -> str:
                wl.interleave, int(np.median(wl.lengths)), int(max(wl.lengths))))
 
 
+KERNEL_SOURCES = ("mla_partial.hip", "gqa_partial.hip", "reduce.hip", "dcp_device.h", "dcp_params.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("mla_partial.hip", "reduce.hip", "dcp_device.h"):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "decode_attention_sequence_paged_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were
-    taken on this workload and on the current kernel source; else None."""
+    """HBM bytes per dcp_decode_partial call from the committed rocprofv3 counter runs,
+    if they were taken on this workload and on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload_name") != workload:
+    if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    w = t.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(wl, budget_s: float):
