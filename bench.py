@@ -12,6 +12,7 @@ Printed as one JSON line:
   rank0_kv_gbps    local-shard KV GB/s of rank 0's partial call (HIP events)
   roofline         the partial-attention call against the 8 TB/s HBM peak
   cpu_baseline     the float64 oracle on the host cores, per-rank partials of the batch
+  hbm_read_probe   attainable HBM read bandwidth of plain streaming loads on this device
 
 With --bands it instead prints one JSON line with rank 0's partial-call bandwidth for
 each request-length band of the pages' comparison by sequence length (<32k, 32-64k,
@@ -216,6 +217,25 @@ def _event_ms(fn, steps: int, warmup: int) -> float:
         b.record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def hbm_read_probe(steps: int, warmup: int, nbytes: int = 4 << 30):
+    """Attainable HBM read bandwidth on this device: the harness's streaming-read probe
+    (plain 16-byte loads) over a buffer larger than the caches, best of two grid sizes."""
+    import torch
+    import dcp_inputs as di
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    best = None
+    for blocks in (1024, 4096):
+        t = _event_ms(lambda: di.hbm_read_probe(buf, sink, blocks), max(steps, 5), max(warmup, 1))
+        gbps = nbytes / (t * 1e-3) / 1e9
+        if best is None or gbps > best[0]:
+            best = (gbps, blocks, t)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"gbps": round(best[0], 1), "bytes": nbytes, "blocks": best[1], "ms": round(best[2], 4),
+            "kind": "streaming read, 16-byte vector loads, 256-thread work-groups, buffer zero-filled"}
 
 
 def run_next(args):
@@ -473,6 +493,11 @@ def main():
             "launch_ms": round(float(t_rank.mean()), 4),
         },
     }
+    del ranks
+    torch.cuda.empty_cache()
+    probe = hbm_read_probe(args.steps, args.warmup)
+    out["hbm_read_probe"] = probe
+    out["roofline"]["frac_of_probe"] = round(achieved / probe["gbps"], 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -353,6 +353,9 @@ def synth_lib() -> ctypes.CDLL:
         lib.dcp_synth_fill_value.restype = ctypes.c_int
         lib.dcp_synth_fill_value.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint16,
                                              ctypes.c_void_p]
+        lib.dcp_hbm_read_probe.restype = ctypes.c_int
+        lib.dcp_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_int32, ctypes.c_void_p]
         _synth_lib = lib
     return _synth_lib
 
@@ -391,3 +394,15 @@ def device_fill_value(dst, bits: int, hip_stream: int = 0) -> None:
                                           ctypes.c_void_p(hip_stream))
     if rc != 0:
         raise RuntimeError("dcp_synth_fill_value failed with code %d" % rc)
+
+
+def hbm_read_probe(buf, sink, blocks: int, hip_stream: int = 0) -> None:
+    """Launch the streaming-read probe over the bytes of the contiguous CUDA tensor
+    ``buf`` (a harness measurement; ``sink`` is a CUDA tensor of >= 1024 int32)."""
+    nbytes = buf.numel() * buf.element_size()
+    assert buf.is_contiguous() and sink.numel() >= 1024
+    rc = synth_lib().dcp_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_int64(nbytes),
+                                        ctypes.c_void_p(sink.data_ptr()), ctypes.c_int32(blocks),
+                                        ctypes.c_void_p(hip_stream))
+    if rc != 0:
+        raise RuntimeError("dcp_hbm_read_probe failed (%d)" % rc)

@@ -23,7 +23,8 @@ def build_all() -> None:
     _run(["/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc",
           "-O3", "-fPIC", "-shared", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          os.path.join(HERE, "csrc", "synth_fill.hip"), "-o", dev + ".tmp"])
+          os.path.join(HERE, "csrc", "synth_fill.hip"), os.path.join(HERE, "csrc", "hbm_probe.hip"),
+          "-o", dev + ".tmp"])
     os.replace(dev + ".tmp", dev)
 
 

@@ -157,8 +157,9 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     DCP_LDS uint8_t* vdst = kdst + C::kHalfBytes;
 #pragma unroll
     for (int k = 0; k < C::kCopies; ++k) {
-      copy16(p.k_cache + src, ld_off[k], lds_addr(kdst + (k * KVW + wave) * 1024));
-      copy16(p.v_cache + src, ld_off[k], lds_addr(vdst + (k * KVW + wave) * 1024));
+      // head groups of a span read disjoint KV heads: every page byte has one reader
+      copy16<true>(p.k_cache + src, ld_off[k], lds_addr(kdst + (k * KVW + wave) * 1024));
+      copy16<true>(p.v_cache + src, ld_off[k], lds_addr(vdst + (k * KVW + wave) * 1024));
     }
   };
 

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     }
   };
   auto issue_copy = [&](int k, int stage) {
-    copy16(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * C::kWaves + wave) * 1024));
+    copy16<true>(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * C::kWaves + wave) * 1024));
   };
 
   // q[b, head0 + 16 hb, 32 (2 s' + kk) + 8 q4 .. +7]: the B operand of S^T = K Q^T
@@ -471,6 +471,8 @@ constexpr int kPfV = 4;                         // V^T operand blocks in flight 
 static_assert(kCopyInstr % kRoleWaves == 0, "copies must split evenly over the P.V waves");
 }  // namespace wide
 
+// kStream: one head group (every page has one reader), see copy16.
+template <bool kStream>
 __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(PartialParams p) {
   using namespace wide;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
@@ -692,7 +694,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
     auto issue_tile = [&](int stage) {
 #pragma unroll
       for (int k = 0; k < kCopies; ++k)
-        copy16(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * kRoleWaves + v) * 1024));
+        copy16<kStream>(src, ld_off[k], lds_addr(lds + stage * kTileBytes + (k * kRoleWaves + v) * 1024));
       if (--lc_left > 0) {
         cursor_next(lc, p, tpp);
         next_src();
@@ -810,8 +812,10 @@ hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;
   if (mla_heads_per_group(p.num_q_heads) == 32)
     hipLaunchKernelGGL(mla::mla_partial_kernel<1>, dim3(grid), dim3(128), 0, stream, p);
-  else
-    hipLaunchKernelGGL(mla::mla_partial_wide_kernel, dim3(grid), dim3(mla::wide::kThreads), 0, stream, p);
+  else if (p.num_head_groups == 1)
+    hipLaunchKernelGGL(mla::mla_partial_wide_kernel<true>, dim3(grid), dim3(mla::wide::kThreads), 0, stream, p);
+  else  // the head groups of a span share its pages through L2
+    hipLaunchKernelGGL(mla::mla_partial_wide_kernel<false>, dim3(grid), dim3(mla::wide::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
