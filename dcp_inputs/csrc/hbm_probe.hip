@@ -1,7 +1,7 @@
-// Streaming-read probe of the bench harness: the HBM read bandwidth that plain
-// 16-byte vector loads attain on this device, as context for the attention
-// kernels' bandwidth.  Every work-group walks the buffer grid-stride with four
-// independent loads in flight per thread; the XOR of what was read decides a
+// Streaming-read probe of the bench harness: the HBM read bandwidth that streaming
+// (non-temporal) 16-byte vector loads attain on this device, as context for the
+// attention kernels' bandwidth.  Every work-group walks the buffer grid-stride with
+// eight independent loads in flight per thread; the XOR of what was read decides a
 // store that never happens for the fill the harness uses, so no load is dropped.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -10,14 +10,18 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void hbm_read_probe_kernel(const u32x4_t* __restrict__ src, int64_t n,
                                                              unsigned* __restrict__ sink) {
+  constexpr int kInFlight = 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   u32x4_t acc = u32x4_t{0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4_t a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+  for (; i + (kInFlight - 1) * stride < n; i += kInFlight * stride) {
+    u32x4_t v[kInFlight];
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) acc ^= v[u];
   }
-  for (; i < n; i += stride) acc ^= src[i];
+  for (; i < n; i += stride) acc ^= __builtin_nontemporal_load(src + i);
   const unsigned x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (x == 0x9E3779B9u) sink[blockIdx.x & 1023] = x;
 }
