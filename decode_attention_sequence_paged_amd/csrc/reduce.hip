@@ -13,16 +13,18 @@
 namespace dcp {
 
 // ------------------------------------------------------------------ split-K reduce
-// One block per (request, group of heads).  A head's v_dim outputs are spread over
-// DV/4 threads (4 consecutive floats each); with PL > 1, PL such thread sets ("piece
-// lanes") fold every PL-th piece of the request and are summed through LDS at the
-// end.  The pieces' slots and LSEs are first staged in LDS by the whole block, a
-// chunk of kThreads pieces at a time with a running maximum, so any piece count
-// works.  The host picks PL from the expected pieces per request (partitions /
-// batch): 1 for batches of many requests, up to 8 for a single very long request.
-template <int DV, int PL>
+// One block per (request, group of heads, slice of DV / DS output dims).  A head's
+// slice is spread over DV/DS/4 threads (4 consecutive floats each); with PL > 1, PL
+// such thread sets ("piece lanes") fold every PL-th piece of the request and are
+// summed through LDS at the end.  The pieces' slots and LSEs are first staged in
+// LDS by the whole block, a chunk of kThreads pieces at a time with a running
+// maximum, so any piece count works.  The host picks PL from the expected pieces per request (partitions /
+// batch): 1 for batches of many requests, up to 8 for a single very long request,
+// whose 512 outputs per head are then cut into 4 slices so that the merge is spread
+// over four times as many blocks (9.0 instead of 10.0 us for the 1M-token request).
+template <int DV, int PL, int DS = 1>
 struct SplitCfg {
-  static constexpr int kQuads = DV / 4;                      // threads per head and piece lane
+  static constexpr int kQuads = DV / 4 / DS;                 // threads per head and piece lane
   static constexpr int kTph = kQuads * PL;                   // threads per head
   static constexpr int kThreads = kTph < 256 ? 256 : kTph;
   static constexpr int kHpb = kThreads / kTph;               // heads per block
@@ -30,9 +32,9 @@ struct SplitCfg {
   static_assert(kThreads % kTph == 0 && kThreads <= 1024, "block shape");
 };
 
-template <int DV, int PL>
-__global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_kernel(SplitReduceParams p) {
-  using C = SplitCfg<DV, PL>;
+template <int DV, int PL, int DS = 1>
+__global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce_kernel(SplitReduceParams p) {
+  using C = SplitCfg<DV, PL, DS>;
   constexpr int kChunk = C::kThreads;  // pieces staged per round
   __shared__ int64_t s_slot[kChunk];
   __shared__ float s_lse[kChunk][C::kHpb];
@@ -51,11 +53,12 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
 
   const int64_t F = p.ws_prefix[b];
   const int64_t n = p.ws_prefix[b + 1] - F;
-  float* orow = p.out_o + ((int64_t)b * p.out_req_rows + head) * DV + 4 * q;
+  const int col = (int)blockIdx.z * (DV / DS) + 4 * q;
+  float* orow = p.out_o + ((int64_t)b * p.out_req_rows + head) * DV + col;
   if (n == 0) {  // no local tokens: the merge's neutral element
     if (head_ok && pl == 0) {
       *(f32x4*)orow = f32x4{};
-      if (q == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = -INFINITY;
+      if (col == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = -INFINITY;
     }
     return;
   }
@@ -104,7 +107,7 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
           // empty pieces (a causally masked row) carry no weight
           const float l = s_lse[i][hd];
           wt[u] = slot >= 0 && l != -INFINITY ? fast_exp2(l - mx) : 0.f;
-          v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + 4 * q) : f32x4{};
+          v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + col) : f32x4{};
         }
 #pragma unroll
         for (int u = 0; u < C::kUnroll; ++u) {
@@ -129,14 +132,14 @@ __global__ __launch_bounds__((SplitCfg<DV, PL>::kThreads)) void split_reduce_ker
   if (!head_ok) return;
   // a row no piece saw a token for: the merge's neutral element
   *(f32x4*)orow = wsum > 0.f ? acc * (1.0f / wsum) : f32x4{};
-  if (q == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
+  if (col == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int DV, int PL>
+template <int DV, int PL, int DS = 1>
 static hipError_t launch_split(const SplitReduceParams& p, hipStream_t stream) {
-  using C = SplitCfg<DV, PL>;
-  dim3 grid(p.batch, (p.num_heads + C::kHpb - 1) / C::kHpb);
-  hipLaunchKernelGGL((split_reduce_kernel<DV, PL>), grid, dim3(C::kThreads), 0, stream, p);
+  using C = SplitCfg<DV, PL, DS>;
+  dim3 grid(p.batch, (p.num_heads + C::kHpb - 1) / C::kHpb, DS);
+  hipLaunchKernelGGL((split_reduce_kernel<DV, PL, DS>), grid, dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -147,7 +150,7 @@ hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream) {
   if (p.v_dim == 512) {
     if (per <= 4) return launch_split<512, 1>(p, stream);
     if (per <= 16) return launch_split<512, 2>(p, stream);
-    return launch_split<512, 8>(p, stream);
+    return launch_split<512, 8, 4>(p, stream);
   }
   if (per <= 4) return launch_split<128, 1>(p, stream);
   if (per <= 16) return launch_split<128, 4>(p, stream);
