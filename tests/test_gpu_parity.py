@@ -592,3 +592,72 @@ def test_mtp_census(name, q_len, kw):
                 got = np.rint(o[b, i][:, :24] * vis.size)
                 assert np.array_equal(got, np.broadcast_to(counts, got.shape)), (r, b, i)
                 assert np.allclose(lse[b, i], math.log(vis.size), atol=1e-4), (r, b, i)
+
+
+# ----------------------------------------------------------------------------- randomized shapes
+
+def _random_case(seed):
+    """A seeded random shape: kind, heads, page size, DCP size and interleave, lengths
+    (including empty and tiny requests), work partitions and query tokens."""
+    rng = np.random.default_rng(1000 + seed)
+    k = seed // 2
+    if seed % 2 == 0:
+        H = (1, 8, 16, 24, 32, 40, 64, 100, 128, 192)[k % 10]
+        kind, Hkv, dq, dv = "mla", 1, 576, 512
+        bs = int(rng.choice([32, 64, 96, 128, 256]))
+        q_len = int(rng.choice([1, 1, 2, 3])) if H <= 128 else 1
+    else:
+        Hkv = (1, 2, 4, 8)[k % 4]
+        H = Hkv * (1, 2, 4, 8, 16)[k % 5]
+        kind, dq, dv = "gqa", 128, 128
+        bs = int(rng.choice([16, 32, 48, 64]))
+        q_len = int(rng.choice([1, 1, 2, 4]))
+    N = int(rng.integers(1, 9))
+    I = int(rng.choice([1, 2, 3, 7, 16, 64, 128, 300]))
+    B = int(rng.integers(1, 7))
+    lengths = tuple(int(x) for x in rng.choice([0, 1, 2, 5, 31, 33, 200, 1000, 2500, 6000], size=B))
+    lengths = tuple(int(min(6000, x + rng.integers(0, 50))) for x in lengths)
+    parts = int(rng.choice([0, 1, 3, 9, 40]))
+    wl = di.Workload("rand%d" % seed, kind, B, H, Hkv, dq, dv, bs, N, I, 100 + seed, lengths)
+    return wl, q_len, parts
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_shapes_every_rank_and_merge(seed):
+    """Seeded random shapes of both kinds (heads, page size, N, I, partitions, lengths
+    with empty and one-token requests, 1-4 query tokens): every rank's partial against
+    the oracle's, and the merge over the ranks against attention over the whole
+    context."""
+    wl, q_len, parts = _random_case(seed)
+    N, B, H, Dv = wl.dcp_size, wl.batch, wl.num_q_heads, wl.v_dim
+    print("case", seed, wl, "q_len", q_len, "parts", parts, flush=True)
+    o_all = torch.empty((N, B, q_len * H, Dv), device="cuda")
+    l_all = torch.empty((N, B, q_len * H), device="cuda")
+    for r in range(N):
+        if q_len == 1:
+            o, lse, _ = run_rank(wl, r, parts=parts)
+            o, lse = o.view(B, 1, H, Dv), lse.view(B, 1, H)
+        else:
+            o, lse = run_rank_mtp(wl, r, q_len, parts=parts)
+        o_all[r] = o.reshape(B, q_len * H, Dv)
+        l_all[r] = lse.reshape(B, q_len * H)
+        on, ln = o.cpu().numpy(), lse.cpu().numpy()
+        for b in range(B):
+            if q_len == 1:
+                o_ref, l_ref = oracle.rank_partial(wl, b, r)
+                o_ref, l_ref = o_ref[None], l_ref[None]
+            else:
+                o_ref, l_ref = oracle.mtp_rank_partial(wl, b, r, q_len)
+            check_close(on[b], ln[b], o_ref, l_ref, "random %d rank %d b=%d" % (seed, r, b))
+    om = torch.empty((B, q_len * H, Dv), device="cuda")
+    lm = torch.empty((B, q_len * H), device="cuda")
+    dcp.dcp_merge(o_all, l_all, om, lm)
+    torch.cuda.synchronize()
+    om, lm = om.view(B, q_len, H, Dv).cpu().numpy(), lm.view(B, q_len, H).cpu().numpy()
+    for b in range(B):
+        if q_len == 1:
+            o_ref, l_ref = oracle.full_attention(wl, b)
+            o_ref, l_ref = o_ref[None], l_ref[None]
+        else:
+            o_ref, l_ref = oracle.mtp_full_attention(wl, b, q_len)
+        check_close(om[b], lm[b], o_ref, l_ref, "random %d merged b=%d" % (seed, b))
