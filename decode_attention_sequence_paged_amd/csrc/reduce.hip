@@ -14,17 +14,19 @@ namespace dcp {
 
 // ------------------------------------------------------------------ split-K reduce
 // One block per (request, group of heads, slice of DV / DS output dims).  A head's
-// slice is spread over DV/DS/4 threads (4 consecutive floats each); with PL > 1, PL
-// such thread sets ("piece lanes") fold every PL-th piece of the request and are
-// summed through LDS at the end.  The pieces' slots and LSEs are first staged in
-// LDS by the whole block, a chunk of kThreads pieces at a time with a running
-// maximum, so any piece count works.  The host picks PL from the expected pieces per request (partitions /
-// batch): 1 for batches of many requests, up to 8 for a single very long request,
-// whose 512 outputs per head are then cut into 4 slices so that the merge is spread
-// over four times as many blocks (9.0 instead of 10.0 us for the 1M-token request).
-template <int DV, int PL, int DS = 1>
+// slice is spread over DV/DS/4/QPT threads, each owning QPT quads of 4 consecutive
+// floats kQStride apart (so a wave's loads stay contiguous); with PL > 1, PL such
+// thread sets ("piece lanes") fold every PL-th piece of the request and are summed
+// through LDS at the end.  The pieces' slots and LSEs are first staged in LDS by the
+// whole block, a chunk of kThreads pieces at a time with a running maximum, so any
+// piece count works.  The host picks PL from the expected pieces per request
+// (partitions / batch): 1 for batches of many requests, up to 8 for a single very
+// long request, whose 512 outputs per head are then cut into 4 slices so that the
+// merge is spread over four times as many blocks (9.0 instead of 10.0 us for the
+// 1M-token request).
+template <int DV, int PL, int DS = 1, int QPT = 1>
 struct SplitCfg {
-  static constexpr int kQuads = DV / 4 / DS;                 // threads per head and piece lane
+  static constexpr int kQuads = DV / 4 / DS / QPT;           // threads per head and piece lane
   static constexpr int kTph = kQuads * PL;                   // threads per head
   static constexpr int kThreads = kTph < 256 ? 256 : kTph;
   static constexpr int kHpb = kThreads / kTph;               // heads per block
@@ -32,9 +34,11 @@ struct SplitCfg {
   static_assert(kThreads % kTph == 0 && kThreads <= 1024, "block shape");
 };
 
-template <int DV, int PL, int DS = 1>
-__global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce_kernel(SplitReduceParams p) {
-  using C = SplitCfg<DV, PL, DS>;
+template <int DV, int PL, int DS = 1, int QPT = 1>
+__global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_reduce_kernel(SplitReduceParams p) {
+  using C = SplitCfg<DV, PL, DS, QPT>;
+  static_assert(PL == 1 || QPT == 1, "quads per thread only without piece lanes");
+  constexpr int kQStride = 4 * C::kQuads;  // floats between a thread's quads
   constexpr int kChunk = C::kThreads;  // pieces staged per round
   __shared__ int64_t s_slot[kChunk];
   __shared__ float s_lse[kChunk][C::kHpb];
@@ -57,7 +61,8 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce
   float* orow = p.out_o + ((int64_t)b * p.out_req_rows + head) * DV + col;
   if (n == 0) {  // no local tokens: the merge's neutral element
     if (head_ok && pl == 0) {
-      *(f32x4*)orow = f32x4{};
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) *(f32x4*)(orow + k * kQStride) = f32x4{};
       if (col == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = -INFINITY;
     }
     return;
@@ -72,7 +77,9 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce
   if (w_lo == w_hi) return;  // computed in one piece by the partial kernel
 
   float mx = -INFINITY, wsum = 0.f;
-  f32x4 acc = f32x4{};
+  f32x4 acc[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) acc[k] = f32x4{};
   for (int64_t base = w_lo; base <= w_hi; base += kChunk) {
     const int cnt = (int)((w_hi - base + 1) < kChunk ? (w_hi - base + 1) : kChunk);
     __syncthreads();  // the previous round's LDS reads are done
@@ -93,12 +100,13 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce
     for (int i = 0; i < cnt; ++i) cm = fmaxf(cm, s_lse[i][hd]);
     const float nm = fmaxf(mx, cm);
     const float rescale = mx == -INFINITY ? 0.f : fast_exp2(mx - nm);
-    acc *= rescale;
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) acc[k] *= rescale;
     wsum *= rescale;
     mx = nm;
     if (head_ok) {
       for (int i0 = pl; i0 < cnt; i0 += PL * C::kUnroll) {
-        f32x4 v[C::kUnroll];
+        f32x4 v[C::kUnroll][QPT];
         float wt[C::kUnroll];
 #pragma unroll
         for (int u = 0; u < C::kUnroll; ++u) {
@@ -107,39 +115,43 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS>::kThreads)) void split_reduce
           // empty pieces (a causally masked row) carry no weight
           const float l = s_lse[i][hd];
           wt[u] = slot >= 0 && l != -INFINITY ? fast_exp2(l - mx) : 0.f;
-          v[u] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + col) : f32x4{};
+#pragma unroll
+          for (int k = 0; k < QPT; ++k)
+            v[u][k] = slot >= 0 ? *(const f32x4*)(p.ws_o + (slot * H + head) * DV + col + k * kQStride) : f32x4{};
         }
 #pragma unroll
         for (int u = 0; u < C::kUnroll; ++u) {
           wsum += wt[u];
-          acc += wt[u] * v[u];
+#pragma unroll
+          for (int k = 0; k < QPT; ++k) acc[k] += wt[u] * v[u][k];
         }
       }
     }
   }
   if constexpr (PL > 1) {  // every piece lane used the same maximum: plain sums
-    s_acc[threadIdx.x] = acc;
+    s_acc[threadIdx.x] = acc[0];
     s_w[threadIdx.x] = wsum;
     __syncthreads();
     if (pl != 0) return;
     const int base = hd * C::kTph + q;
 #pragma unroll
     for (int j = 1; j < PL; ++j) {
-      acc += s_acc[base + j * C::kQuads];
+      acc[0] += s_acc[base + j * C::kQuads];
       wsum += s_w[base + j * C::kQuads];
     }
   }
   if (!head_ok) return;
   // a row no piece saw a token for: the merge's neutral element
-  *(f32x4*)orow = wsum > 0.f ? acc * (1.0f / wsum) : f32x4{};
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) *(f32x4*)(orow + k * kQStride) = wsum > 0.f ? acc[k] * (1.0f / wsum) : f32x4{};
   if (col == 0) p.out_lse[(int64_t)b * p.out_req_rows + head] = wsum > 0.f ? (mx + fast_log2(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int DV, int PL, int DS = 1>
+template <int DV, int PL, int DS = 1, int QPT = 1>
 static hipError_t launch_split(const SplitReduceParams& p, hipStream_t stream) {
-  using C = SplitCfg<DV, PL, DS>;
+  using C = SplitCfg<DV, PL, DS, QPT>;
   dim3 grid(p.batch, (p.num_heads + C::kHpb - 1) / C::kHpb, DS);
-  hipLaunchKernelGGL((split_reduce_kernel<DV, PL, DS>), grid, dim3(C::kThreads), 0, stream, p);
+  hipLaunchKernelGGL((split_reduce_kernel<DV, PL, DS, QPT>), grid, dim3(C::kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -147,12 +159,15 @@ hipError_t launch_split_reduce(const SplitReduceParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
   // Expected pieces per request: about partitions / batch + 1.
   const int64_t per = (int64_t)p.num_parts / p.batch + 1;
+  // Many requests: two quads per thread halve the waves of the grid (measured 25.6 ->
+  // 19.1 us at B = 512; at B = 128 one quad per thread is faster, 16.8 against 21.7 us).
+  const bool big = p.batch >= 256;
   if (p.v_dim == 512) {
-    if (per <= 4) return launch_split<512, 1>(p, stream);
+    if (per <= 4) return big ? launch_split<512, 1, 1, 2>(p, stream) : launch_split<512, 1>(p, stream);
     if (per <= 16) return launch_split<512, 2>(p, stream);
     return launch_split<512, 8, 4>(p, stream);
   }
-  if (per <= 4) return launch_split<128, 1>(p, stream);
+  if (per <= 4) return big ? launch_split<128, 1, 1, 2>(p, stream) : launch_split<128, 1>(p, stream);
   if (per <= 16) return launch_split<128, 4>(p, stream);
   return launch_split<128, 16>(p, stream);
 }

@@ -661,3 +661,33 @@ def test_random_shapes_every_rank_and_merge(seed):
         else:
             o_ref, l_ref = oracle.mtp_full_attention(wl, b, q_len)
         check_close(om[b], lm[b], o_ref, l_ref, "random %d merged b=%d" % (seed, b))
+
+
+@pytest.mark.parametrize("kind", ["mla", "gqa"])
+def test_many_short_requests_every_request(kind):
+    """A batch of 300 short requests (the split reduce then gives each thread two output
+    quads): every request of both ranks against the oracle, and the merge."""
+    rng = np.random.default_rng(7)
+    lengths = tuple(int(x) for x in rng.integers(0, 1500, size=300))
+    if kind == "mla":
+        wl = di.Workload("many_mla", "mla", 300, 64, 1, 576, 512, 64, 2, 16, 31, lengths)
+    else:
+        wl = di.Workload("many_gqa", "gqa", 300, 32, 4, 128, 128, 16, 2, 3, 32, lengths)
+    N, B, H, Dv = wl.dcp_size, wl.batch, wl.num_q_heads, wl.v_dim
+    o_all = torch.empty((N, B, H, Dv), device="cuda")
+    l_all = torch.empty((N, B, H), device="cuda")
+    for r in range(N):
+        o, lse, _ = run_rank(wl, r)
+        o_all[r], l_all[r] = o, lse
+        on, ln = o.cpu().numpy(), lse.cpu().numpy()
+        for b in range(B):
+            Or, Lr = oracle_rank(wl, b, r)
+            check_close(on[b], ln[b], Or, Lr, "many %s r%d b%d" % (kind, r, b))
+    om = torch.empty((B, H, Dv), device="cuda")
+    lm = torch.empty((B, H), device="cuda")
+    dcp.dcp_merge(o_all, l_all, om, lm)
+    torch.cuda.synchronize()
+    om, lm = om.cpu().numpy(), lm.cpu().numpy()
+    for b in range(B):
+        Of, Lf = oracle.full_attention(wl, b)
+        check_close(om[b], lm[b], Of, Lf, "many %s merged b%d" % (kind, b))
