@@ -150,6 +150,38 @@ def test_merge_kernel_against_oracle():
         assert np.all(og[~fin] == 0)
 
 
+def test_merge_kernel_large_partials_against_oracle():
+    """Stacked partials larger than the last-level cache (12 parts of [128, 128, 512]
+    fp32, 403 MB: the streaming merge, two chunks of up to 8 parts), empty parts
+    poisoned with NaN, checked against the oracle's merge on sampled rows."""
+    N, B, H, Dv = 12, 128, 128, 512
+    g = torch.Generator(device="cuda").manual_seed(9)
+    O = torch.randn((N, B, H, Dv), device="cuda", generator=g)
+    L = torch.randn((N, B, H), device="cuda", generator=g) * 20
+    drop = torch.rand((N, B, H), device="cuda", generator=g) < 0.3
+    L[drop] = -float("inf")
+    L[:, 0, 0] = -float("inf")                                 # an all-empty row
+    O[drop] = float("nan")                                     # empty parts must carry no weight
+    O[:, 0, 0] = float("nan")
+    og = torch.empty((B, H, Dv), device="cuda")
+    lg = torch.empty((B, H), device="cuda")
+    dcp.dcp_merge(O, L, og, lg)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    rows = [(0, 0), (B - 1, H - 1)] + [tuple(x) for x in zip(rng.integers(0, B, 62), rng.integers(0, H, 62))]
+    for b, h in rows:
+        Lr = L[:, b, h].cpu().numpy().astype(np.float64)
+        Or = O[:, b, h].cpu().numpy().astype(np.float64)
+        Or[np.isneginf(Lr)] = 0.0
+        o_ref, l_ref = oracle.merge(Or, Lr)
+        o_g, l_g = og[b, h].cpu().numpy(), float(lg[b, h])
+        if np.isneginf(l_ref):
+            assert np.isneginf(l_g) and np.all(o_g == 0), (b, h)
+            continue
+        assert np.allclose(o_g, o_ref, rtol=1e-5, atol=1e-5), (b, h)
+        assert abs(l_g - l_ref) <= 1e-5 + 1e-6 * abs(l_ref), (b, h)
+
+
 # ----------------------------------------------------------------------------- configurations
 
 @pytest.mark.parametrize("parts", [0, 1, 5, 16, 64])
