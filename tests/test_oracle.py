@@ -315,11 +315,31 @@ def check_mtp_sharded_merge_equals_unsharded(impl):
         assert np.allclose(O, Ou, rtol=1e-12, atol=1e-13) and np.allclose(LSE, Lu, atol=1e-13)
 
 
+def check_mtp_query_is_a_shorter_request(impl):
+    """On every rank, the causal set of query i of a length-L request with Q query tokens
+    is the rank's shard of a request of length L - (Q - 1 - i): its causal partial equals
+    the single-token partial over that shorter request's tokens on the rank."""
+    rng = np.random.default_rng(14)
+    q, K, V, sc = _mtp_case(rng, Q=4, H=6, Hkv=3, L=37)
+    L, Q = K.shape[0], q.shape[0]
+    for N, I in ((1, 1), (3, 2), (4, 5)):
+        for r in range(N):
+            toks = impl.rank_tokens(L, N, I, r)
+            O, LSE = impl.causal_attention(q, K[toks], V[toks], toks, impl.causal_limits(L, Q), sc)
+            for i in range(Q):
+                short = impl.rank_tokens(L - (Q - 1 - i), N, I, r)
+                Os, Ls = impl.attention(q[i], K[short], V[short], sc)
+                assert np.allclose(O[i], Os, rtol=1e-13, atol=1e-14), (N, I, r, i)
+                assert np.array_equal(np.isneginf(LSE[i]), np.isneginf(Ls))
+                fin = np.isfinite(Ls)
+                assert np.allclose(LSE[i][fin], Ls[fin], atol=1e-13), (N, I, r, i)
+
+
 ALL_CHECKS = [check_contiguous_example, check_one_nth, check_partition, check_against_torch_sdpa,
               check_closed_forms, check_brute_force, check_merge_equals_unsharded,
               check_merge_identities, check_large_logits, check_mtp_single_query_is_decode,
               check_mtp_brute_force, check_mtp_closed_form_counts,
-              check_mtp_sharded_merge_equals_unsharded]
+              check_mtp_sharded_merge_equals_unsharded, check_mtp_query_is_a_shorter_request]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
