@@ -85,7 +85,7 @@ struct WsLayout {
 WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   WsLayout l;
   l.prefix = 256;
-  l.lse = l.prefix + align256(sizeof(int64_t) * 2 * ((size_t)batch + 1));
+  l.lse = l.prefix + align256(sizeof(int64_t) * (3 * (size_t)batch + 2));
   l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
   l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);
   return l;
@@ -274,6 +274,8 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   p.part.num_parts = parts;
   p.part.req_weight = request_weight(&d);
   p.part.len_offset = 0;
+  // span w runs on XCD w % 8 with one head group (see block_to_span)
+  p.part.xcd_weighted = (groups == 1 && parts % 8 == 0) ? 1 : 0;
   p.out_o = out_o;
   p.out_lse = out_lse;
   p.q_req_stride = (int64_t)d.num_q_heads * d.qk_dim;
@@ -292,6 +294,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   r.num_parts = parts;
   r.req_weight = p.part.req_weight;
   r.out_req_rows = d.num_q_heads;
+  r.xcd_weighted = p.part.xcd_weighted;
   r.out_o = out_o;
   r.out_lse = out_lse;
 

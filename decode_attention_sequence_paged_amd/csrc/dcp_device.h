@@ -126,12 +126,34 @@ __device__ __forceinline__ int64_t part_tiles(const PartitionArgs& a, int b) {
   return (part_local_len(a, b) + a.tile - 1) / a.tile;
 }
 
-// Weighted start of span w.
-__device__ __forceinline__ int64_t span_start(int64_t w, int64_t WT, int64_t P) { return w * WT / P; }
+// XCD-weighted spans: when span w runs on XCD w % 8 (one head group, P % 8 == 0), the
+// work-groups of the odd XCDs stream 5-7% slower than those of the even ones (measured
+// in every call, on every box tried), so an odd-XCD span gets kSpanOdd / kSpanEven of
+// an even one's work.  Span w then starts at unit U(w) of U(P) units.
+constexpr int64_t kSpanEven = 17, kSpanOdd = 16, kSpanGroup = 4 * (kSpanEven + kSpanOdd);
+__device__ __forceinline__ int64_t span_units(int64_t w, bool weighted) {
+  if (!weighted) return w;
+  const int64_t j = w & 7;
+  return (w >> 3) * kSpanGroup + kSpanEven * ((j + 1) >> 1) + kSpanOdd * (j >> 1);
+}
 
-// The span that holds weighted position x (0 <= x < WT).
-__device__ __forceinline__ int64_t span_of(int64_t x, int64_t WT, int64_t P) {
-  return ((x + 1) * P - 1) / WT;
+// Weighted start of span w.
+__device__ __forceinline__ int64_t span_start(int64_t w, int64_t WT, int64_t P, bool weighted) {
+  return span_units(w, weighted) * WT / span_units(P, weighted);
+}
+
+// The span that holds weighted position x (0 <= x < WT): the last w with
+// span_start(w) <= x, i.e. with U(w) <= ((x + 1) U(P) - 1) / WT.
+__device__ __forceinline__ int64_t span_of(int64_t x, int64_t WT, int64_t P, bool weighted) {
+  const int64_t umax = ((x + 1) * span_units(P, weighted) - 1) / WT;
+  if (!weighted) return umax;
+  const int64_t g = umax / kSpanGroup, r = umax - g * kSpanGroup;
+  int64_t j = 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k)
+    if (kSpanEven * ((k + 1) >> 1) + kSpanOdd * (k >> 1) <= r) j = k;
+  const int64_t w = g * 8 + j;
+  return w < P ? w : P - 1;
 }
 
 constexpr int kCountBits = 17;  // packed scan value: tiles << kCountBits | requests with tiles
@@ -146,8 +168,10 @@ struct SpanLoc {
 
 // Block-cooperative: every thread of the block gets the location of span w.  If
 // prefix_out is non-null, the block also writes each request's first tile index
-// (prefix_out[b], the total at prefix_out[B]) and weighted position (prefix_out[B +
-// 1 + b], the weighted total at prefix_out[2 B + 1]).  s_scan must hold blockDim.x / 64
+// (prefix_out[b], the total at prefix_out[B]), weighted position (prefix_out[B + 1 +
+// b], the weighted total at prefix_out[2 B + 1]) and the spans of its first and last
+// tiles (prefix_out[2 B + 2 + b] = w_first << 32 | w_last; 0 for a request without
+// tiles), so that the split reduce need not repeat the partition arithmetic.  s_scan must hold blockDim.x / 64
 // int64 values; s_loc four int64 values.
 template <int NT>
 __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
@@ -186,15 +210,25 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
   const int64_t A = a.req_weight;
   const int64_t TT = tot >> kCountBits;
   const int64_t WT = TT + A * (tot & kCountMask);
-  const int64_t x0 = span_start(w, WT, a.num_parts);
-  const int64_t x1 = span_start(w + 1, WT, a.num_parts);
+  const int64_t x0 = span_start(w, WT, a.num_parts, a.xcd_weighted);
+  const int64_t x1 = span_start(w + 1, WT, a.num_parts, a.xcd_weighted);
   // Walk this thread's requests; the one whose weighted range holds x0 (x1) gives
   // the span's first (end) tile.
   int64_t F = excl >> kCountBits;
   int64_t WP = F + A * (excl & kCountMask);
   for (int b = b_lo; b < b_hi; ++b) {
     const int64_t n = part_tiles(a, b);
-    if (prefix_out) { prefix_out[b] = F; prefix_out[a.batch + 1 + b] = WP; }
+    if (prefix_out) {
+      prefix_out[b] = F;
+      prefix_out[a.batch + 1 + b] = WP;
+      int64_t span_range = 0;
+      if (n > 0) {
+        const int64_t wf = span_of(WP + A, WT, a.num_parts, a.xcd_weighted);
+        const int64_t wl = span_of(WP + A + n - 1, WT, a.num_parts, a.xcd_weighted);
+        span_range = (wf << 32) | wl;
+      }
+      prefix_out[2 * a.batch + 2 + b] = span_range;
+    }
     if (n > 0) {
       const int64_t wend = WP + A + n;
       if (x0 < x1 && WP <= x0 && x0 < wend) {

@@ -15,6 +15,7 @@ struct PartitionArgs {
   int32_t num_parts;        // P
   int32_t req_weight;       // tiles of work charged to each request with local tokens
   int32_t len_offset;       // subtracted from every seq_lens entry (a query token's causal length)
+  int32_t xcd_weighted;     // spans weighted by the speed of the XCD they run on (see span_units)
 };
 
 struct PartialParams {
@@ -35,17 +36,19 @@ struct PartialParams {
   int64_t q_req_stride;     // GQA: query elements between consecutive requests (H * qk_dim unless a
                             // query token of a multi-token batch)
   int64_t out_req_rows;     // GQA: output rows between consecutive requests (H unless likewise)
-  int64_t* ws_prefix;       // [2 (B + 1)]: tile prefix, then weighted prefix
+  int64_t* ws_prefix;       // [3 B + 2]: tile prefix, weighted prefix, span range of each request
   float* ws_lse;            // [2P, H]
   float* ws_o;              // [2P, H, v_dim]
 };
 
 struct SplitReduceParams {
-  const int64_t* ws_prefix;  // [2 (B + 1)]: first tile of each request (total at [B]), then
-                             // its weighted position (weighted total at [2 B + 1])
+  const int64_t* ws_prefix;  // [3 B + 2]: first tile of each request (total at [B]), its
+                             // weighted position (weighted total at [2 B + 1]), then the
+                             // spans of its first and last tiles (w_first << 32 | w_last)
   const float* ws_lse;       // [2P, H]
   const float* ws_o;         // [2P, H, v_dim]
   int32_t batch, num_heads, v_dim, num_parts, req_weight;
+  int32_t xcd_weighted;      // as PartitionArgs::xcd_weighted of the partial call
   int64_t out_req_rows;      // output rows between consecutive requests (num_heads, or q_len *
                              // num_heads for one query token of a multi-token GQA batch)
   float* out_o;              // [B, H, v_dim]

@@ -55,8 +55,13 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_r
   const int H = p.num_heads;
   const bool head_ok = head < H;
 
+  // the request's partition entry, read in one round: first tile, tile count, weighted
+  // position, weighted total, and the spans of its first and last tiles
   const int64_t F = p.ws_prefix[b];
   const int64_t n = p.ws_prefix[b + 1] - F;
+  const int64_t WP = p.ws_prefix[p.batch + 1 + b];
+  const int64_t WT = p.ws_prefix[2 * p.batch + 1];
+  const int64_t span_range = p.ws_prefix[2 * p.batch + 2 + b];
   const int col = (int)blockIdx.z * (DV / DS) + 4 * q;
   float* orow = p.out_o + ((int64_t)b * p.out_req_rows + head) * DV + col;
   if (n == 0) {  // no local tokens: the merge's neutral element
@@ -67,13 +72,10 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_r
     }
     return;
   }
-  // weighted positions of the request's first and last tiles
-  const int64_t WP = p.ws_prefix[p.batch + 1 + b];
-  const int64_t WT = p.ws_prefix[2 * p.batch + 1];
-  const int64_t xF = WP + p.req_weight;
   const int64_t P = p.num_parts;
-  const int64_t w_lo = span_of(xF, WT, P);
-  const int64_t w_hi = span_of(xF + n - 1, WT, P);
+  const bool xw = p.xcd_weighted != 0;
+  const int64_t w_lo = span_range >> 32;
+  const int64_t w_hi = span_range & 0xFFFFFFFF;
   if (w_lo == w_hi) return;  // computed in one piece by the partial kernel
 
   float mx = -INFINITY, wsum = 0.f;
@@ -85,8 +87,8 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_r
     __syncthreads();  // the previous round's LDS reads are done
     for (int i = threadIdx.x; i < cnt; i += C::kThreads) {
       const int64_t w = base + i;
-      const int64_t x0 = span_start(w, WT, P);
-      const bool empty = x0 == span_start(w + 1, WT, P);  // an empty span holds no piece
+      const int64_t x0 = span_start(w, WT, P, xw);
+      const bool empty = x0 == span_start(w + 1, WT, P, xw);  // an empty span holds no piece
       // The first span may start before the request (it is that span's last piece);
       // every later one starts inside it (its first piece).
       const int64_t slot = empty ? -1 : 2 * w + (w == w_lo && x0 < WP ? 1 : 0);
