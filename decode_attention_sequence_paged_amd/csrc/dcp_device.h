@@ -107,8 +107,9 @@ __device__ __forceinline__ T ld_const(const T* ptr) {
 // memory traffic), so each request with local tokens is charged A extra tiles,
 // placed in front of its own: request b occupies the weighted range [WP_b,
 // WP_(b+1)) with WP_(b+1) = WP_b + A + n_b, and its tile k sits at WP_b + A + k.
-// Span w covers the weighted range [floor(w*WT/P), floor((w+1)*WT/P)), WT being the
-// weighted total, i.e. the tiles whose weighted positions fall into it; a span
+// Span w covers the weighted range [floor(U(w)*WT/U(P)), floor(U(w+1)*WT/U(P))), WT
+// being the weighted total and U(w) = w unless the spans are XCD-weighted (see
+// span_units), i.e. the tiles whose weighted positions fall into it; a span
 // boundary inside a request's charge moves to that request's first tile.  A request
 // whose tiles fall into several spans is computed piecewise; each piece writes a
 // partial (O, LSE) into a workspace slot and a second kernel merges them.  Span w
