@@ -22,6 +22,7 @@ import pytest
 import scipy.special
 import torch
 
+import dcp_inputs as di
 import oracle
 from oracle import dcp_oracle as odc
 
@@ -48,12 +49,15 @@ def _rand_case(rng, H=8, Hkv=2, L=37, D=24, Dv=16):
 class Impl:
     def __init__(self, attention=oracle.attention, merge=oracle.merge,
                  rank_tokens=oracle.rank_tokens, causal_attention=oracle.causal_attention,
-                 causal_limits=oracle.causal_limits):
+                 causal_limits=oracle.causal_limits, request_inputs=oracle.request_inputs,
+                 mtp_query=oracle.mtp_query):
         self.attention = attention
         self.merge = merge
         self.rank_tokens = rank_tokens
         self.causal_attention = causal_attention
         self.causal_limits = causal_limits
+        self.request_inputs = request_inputs
+        self.mtp_query = mtp_query
 
 
 # ----------------------------------------------------------------------------- pins
@@ -335,11 +339,89 @@ def check_mtp_query_is_a_shorter_request(impl):
                 assert np.allclose(LSE[i][fin], Ls[fin], atol=1e-13), (N, I, r, i)
 
 
+# ----------------------------------------------------------------------------- input readings
+#
+# Which generated values the oracle takes as q, K and V.  The expectations below are
+# built straight from the seeded generator's logical rows (the row-id convention of
+# dcp_inputs: query row b*H + h, latent row b*2**21 + t, GQA row (b*2**21 + t)*Hkv + g)
+# and the readings of the pages: MLA's K is the whole 576-dim latent row and V its first
+# 512 entries (one latent vector shared by every head, blog Sec. 5.3); GQA query head h
+# reads KV head h // (H / Hkv) (blog Sec. 5.4), K from the K stream and V from the V
+# stream.  Two closed forms pin them: q = 0 gives O = the mean of the V rows, and a
+# single cached token gives LSE = scale * q . k over every K dimension.
+
+def _gen(row_ids, cols, seed, stream):
+    return di.bf16_bits_to_f64(di.host_rows(np.asarray(row_ids, dtype=np.uint64), cols, seed, stream))
+
+
+def _latent_row(b, t):
+    return b * (1 << 21) + t
+
+
+def check_mla_input_reading(impl):
+    wl = di.Workload("pin_mla", "mla", 3, 4, 1, 576, 512, 64, 3, 2, 41, (37, 5, 80))
+    H, sc = wl.num_q_heads, wl.softmax_scale
+    for b, toks in ((0, np.array([0, 1, 6, 7, 12, 30, 36])), (1, np.array([2, 3])),
+                    (2, np.arange(0, 80, 3))):
+        rows = _gen([_latent_row(b, int(t)) for t in toks], 576, wl.seed, di.STREAM_K)
+        q, K, V = impl.request_inputs(wl, b, toks)
+        O, LSE = impl.attention(np.zeros_like(q), K, V, sc)
+        assert np.allclose(LSE, math.log(toks.size), atol=1e-13)
+        for h in range(H):
+            assert np.allclose(O[h], rows[:, :512].mean(axis=0), rtol=1e-13, atol=1e-14), (b, h)
+        qrows = _gen([b * H + h for h in range(H)], 576, wl.seed, di.STREAM_Q)
+        for j, t in enumerate(toks[:3]):
+            q1, K1, V1 = impl.request_inputs(wl, b, np.array([t]))
+            O1, L1 = impl.attention(q1, K1, V1, sc)
+            for h in range(H):
+                assert abs(L1[h] - sc * float(qrows[h] @ rows[j])) < 1e-12, (b, t, h)
+                assert np.array_equal(O1[h], rows[j, :512]), (b, t, h)
+
+
+def check_gqa_input_reading(impl):
+    wl = di.Workload("pin_gqa", "gqa", 2, 8, 4, 128, 128, 16, 2, 1, 42, (30, 7))
+    H, Hkv, sc = wl.num_q_heads, wl.num_kv_heads, wl.softmax_scale
+    G = H // Hkv
+    for b, toks in ((0, np.array([0, 2, 5, 17, 29])), (1, np.array([1, 6]))):
+        q, K, V = impl.request_inputs(wl, b, toks)
+        O, LSE = impl.attention(np.zeros_like(q), K, V, sc)
+        assert np.allclose(LSE, math.log(toks.size), atol=1e-13)
+        qrows = _gen([b * H + h for h in range(H)], 128, wl.seed, di.STREAM_Q)
+        for h in range(H):
+            g = h // G
+            ids = [_latent_row(b, int(t)) * Hkv + g for t in toks]
+            vrows = _gen(ids, 128, wl.seed, di.STREAM_V)
+            krows = _gen(ids, 128, wl.seed, di.STREAM_K)
+            assert np.allclose(O[h], vrows.mean(axis=0), rtol=1e-13, atol=1e-14), (b, h)
+            q1, K1, V1 = impl.request_inputs(wl, b, toks[:1])
+            O1, L1 = impl.attention(q1, K1, V1, sc)
+            assert abs(L1[h] - sc * float(qrows[h] @ krows[0])) < 1e-12, (b, h)
+            assert np.array_equal(O1[h], vrows[0]), (b, h)
+
+
+def check_mtp_query_reading(impl):
+    """Query token i of request b is the generator's query row (b*q_len + i)*H + h, the
+    batch of B*q_len single-token queries viewed as [B, q_len, H]: one cached token
+    gives LSE = scale * q . k for every (query token, head)."""
+    wl = di.Workload("pin_mtp", "mla", 2, 3, 1, 576, 512, 64, 1, 1, 43, (9, 4))
+    H, sc, Q = wl.num_q_heads, wl.softmax_scale, 3
+    for b in range(2):
+        krow = _gen([_latent_row(b, 0)], 576, wl.seed, di.STREAM_K)
+        q = impl.mtp_query(wl, b, Q)
+        O, LSE = impl.causal_attention(q, krow[:, None, :], krow[:, None, :512], np.array([0]),
+                                       np.zeros(Q, dtype=np.int64), sc)
+        for i in range(Q):
+            qrows = _gen([(b * Q + i) * H + h for h in range(H)], 576, wl.seed, di.STREAM_Q)
+            for h in range(H):
+                assert abs(LSE[i, h] - sc * float(qrows[h] @ krow[0])) < 1e-12, (b, i, h)
+
+
 ALL_CHECKS = [check_contiguous_example, check_one_nth, check_partition, check_against_torch_sdpa,
               check_closed_forms, check_brute_force, check_merge_equals_unsharded,
               check_merge_identities, check_large_logits, check_mtp_single_query_is_decode,
               check_mtp_brute_force, check_mtp_closed_form_counts,
-              check_mtp_sharded_merge_equals_unsharded, check_mtp_query_is_a_shorter_request]
+              check_mtp_sharded_merge_equals_unsharded, check_mtp_query_is_a_shorter_request,
+              check_mla_input_reading, check_gqa_input_reading, check_mtp_query_reading]
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
@@ -439,6 +521,48 @@ def _mut_limits(kind):
     return lim
 
 
+def _mut_inputs(kind):
+    """Wrong readings of which generated values are q, K and V."""
+    def inputs(wl, b, tokens, seed=None):
+        seed = wl.seed if seed is None else seed
+        t = np.asarray(tokens, dtype=np.int64)
+        H = wl.num_q_heads
+        qid = [h * wl.batch + b for h in range(H)] if kind == "q_transposed" else \
+            [b * H + h for h in range(H)]
+        q = _gen(qid, wl.qk_dim, seed, di.STREAM_Q)
+        if wl.kind == "mla":
+            lat = _gen([_latent_row(b, int(x)) for x in t], wl.qk_dim, seed, di.STREAM_K)
+            K = lat.copy()
+            V = lat[:, :wl.v_dim]
+            if kind == "v_tail":          # V = the last 512 entries (row[64:])
+                V = lat[:, -wl.v_dim:]
+            if kind == "k_no_rope":       # K = the first 512 entries only
+                K[:, wl.v_dim:] = 0.0
+            return q, K[:, None, :], V[:, None, :]
+        Hkv = wl.num_kv_heads
+        g = np.arange(Hkv)
+        if kind == "kv_head_reversed":    # query heads read the groups' KV heads in reverse
+            g = g[::-1]
+        ids = (np.array([_latent_row(b, int(x)) for x in t], dtype=np.int64)[:, None] * Hkv
+               + g[None, :]).reshape(-1)
+        if kind == "kv_rows_transposed":  # KV head major instead of token major
+            ids = ((b * Hkv + np.arange(Hkv))[None, :] * (1 << 21) + t[:, None]).reshape(-1)
+        ks, vs = (di.STREAM_V, di.STREAM_K) if kind == "kv_swapped" else (di.STREAM_K, di.STREAM_V)
+        K = _gen(ids, wl.qk_dim, seed, ks).reshape(t.size, Hkv, wl.qk_dim)
+        V = _gen(ids, wl.v_dim, seed, vs).reshape(t.size, Hkv, wl.v_dim)
+        return q, K, V
+    return inputs
+
+
+def _mut_mtp_query(kind):
+    def mq(wl, b, q_len, seed=None):
+        seed = wl.seed if seed is None else seed
+        H = wl.num_q_heads
+        rows = [(i * wl.batch + b) * H + h for i in range(q_len) for h in range(H)]
+        return _gen(rows, wl.qk_dim, seed, di.STREAM_Q).reshape(q_len, H, wl.qk_dim)
+    return mq
+
+
 MUTANTS = (
     [("attention:" + k, Impl(attention=_mut_attention(k))) for k in
      ["group_mod", "no_scale", "sign", "v_offset", "unnormalised", "lse_no_max", "lse_log2", "drop_last"]]
@@ -449,6 +573,10 @@ MUTANTS = (
     + [("causal:" + k, Impl(causal_attention=_mut_causal(k))) for k in
        ["strict", "local_index", "query_reversed"]]
     + [("limits:" + k, Impl(causal_limits=_mut_limits(k))) for k in ["shift", "no_mask"]]
+    + [("inputs:" + k, Impl(request_inputs=_mut_inputs(k))) for k in
+       ["q_transposed", "v_tail", "k_no_rope", "kv_head_reversed", "kv_rows_transposed",
+        "kv_swapped"]]
+    + [("mtp_query:query_major", Impl(mtp_query=_mut_mtp_query("query_major")))]
 )
 
 
