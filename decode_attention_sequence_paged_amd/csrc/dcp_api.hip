@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/dcp.h"
 #include "dcp_internal.h"
 #include "dcp_params.h"
@@ -20,16 +22,20 @@ constexpr int64_t kMaxMtpRows = kMaxMlaRows;
 constexpr int32_t kMaxGqaQueryTokens = 64;  // query tokens per request of a GQA multi-token call
 constexpr int32_t kMaxDevices = 64;
 
-// Read-only cache of the compute-unit count per device (filled on first use).
-int g_cu_count[kMaxDevices];
+// Cache of the compute-unit count per device (filled on first use; concurrent callers
+// may both fill an entry, with the same value).
+std::atomic<int> g_cu_count[kMaxDevices];
 
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < kMaxDevices && g_cu_count[dev] > 0) return g_cu_count[dev];
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (dev < kMaxDevices) g_cu_count[dev] = cus;
+  if (dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -117,7 +123,7 @@ dcp_status_t hip_status(hipError_t e) { return e == hipSuccess ? DCP_SUCCESS : D
 
 extern "C" {
 
-const char* dcp_status_string(int32_t status) {
+const char* dcp_status_string(dcp_status_t status) {
   switch (status) {
     case DCP_SUCCESS: return "DCP_SUCCESS";
     case DCP_ERROR_INVALID_VALUE: return "DCP_ERROR_INVALID_VALUE";

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "dcp_params.h"
+#include "dcp_partition.h"
 #include "dcp_shard.h"
 
 #define DCP_LDS __attribute__((address_space(3)))
@@ -100,20 +101,8 @@ __device__ __forceinline__ T ld_const(const T* ptr) {
 
 // ------------------------------------------------------------------ work partitions
 //
-// A rank's local tokens of the whole batch are cut into tiles of T tokens (a tile
-// never crosses a request), and the concatenated tile sequence into P spans of
-// equal work.  Besides its tiles, every request a work-group touches costs it the
-// query slice and the output row it writes (for 64 MLA heads, about five tiles of
-// memory traffic), so each request with local tokens is charged A extra tiles,
-// placed in front of its own: request b occupies the weighted range [WP_b,
-// WP_(b+1)) with WP_(b+1) = WP_b + A + n_b, and its tile k sits at WP_b + A + k.
-// Span w covers the weighted range [floor(U(w)*WT/U(P)), floor(U(w+1)*WT/U(P))), WT
-// being the weighted total and U(w) = w unless the spans are XCD-weighted (see
-// span_units), i.e. the tiles whose weighted positions fall into it; a span
-// boundary inside a request's charge moves to that request's first tile.  A request
-// whose tiles fall into several spans is computed piecewise; each piece writes a
-// partial (O, LSE) into a workspace slot and a second kernel merges them.  Span w
-// owns slots 2w (its first request piece) and 2w+1 (its last).
+// How a rank's tiles are cut into spans of equal work, and which workspace slot each
+// request piece takes: dcp_partition.h (shared with the host tests).
 
 // Local length of request b actually processed (clamped to what its block table row holds).
 __device__ __forceinline__ int64_t part_local_len(const PartitionArgs& a, int b) {
@@ -125,36 +114,6 @@ __device__ __forceinline__ int64_t part_local_len(const PartitionArgs& a, int b)
 
 __device__ __forceinline__ int64_t part_tiles(const PartitionArgs& a, int b) {
   return (part_local_len(a, b) + a.tile - 1) / a.tile;
-}
-
-// XCD-weighted spans: when span w runs on XCD w % 8 (one head group, P % 8 == 0), the
-// work-groups of the odd XCDs stream 5-7% slower than those of the even ones (measured
-// in every call, on every box tried), so an odd-XCD span gets kSpanOdd / kSpanEven of
-// an even one's work.  Span w then starts at unit U(w) of U(P) units.
-constexpr int64_t kSpanEven = 17, kSpanOdd = 16, kSpanGroup = 4 * (kSpanEven + kSpanOdd);
-__device__ __forceinline__ int64_t span_units(int64_t w, bool weighted) {
-  if (!weighted) return w;
-  const int64_t j = w & 7;
-  return (w >> 3) * kSpanGroup + kSpanEven * ((j + 1) >> 1) + kSpanOdd * (j >> 1);
-}
-
-// Weighted start of span w.
-__device__ __forceinline__ int64_t span_start(int64_t w, int64_t WT, int64_t P, bool weighted) {
-  return span_units(w, weighted) * WT / span_units(P, weighted);
-}
-
-// The span that holds weighted position x (0 <= x < WT): the last w with
-// span_start(w) <= x, i.e. with U(w) <= ((x + 1) U(P) - 1) / WT.
-__device__ __forceinline__ int64_t span_of(int64_t x, int64_t WT, int64_t P, bool weighted) {
-  const int64_t umax = ((x + 1) * span_units(P, weighted) - 1) / WT;
-  if (!weighted) return umax;
-  const int64_t g = umax / kSpanGroup, r = umax - g * kSpanGroup;
-  int64_t j = 0;
-#pragma unroll
-  for (int k = 1; k < 8; ++k)
-    if (kSpanEven * ((k + 1) >> 1) + kSpanOdd * (k >> 1) <= r) j = k;
-  const int64_t w = g * 8 + j;
-  return w < P ? w : P - 1;
 }
 
 constexpr int kCountBits = 17;  // packed scan value: tiles << kCountBits | requests with tiles
@@ -211,8 +170,8 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
   const int64_t A = a.req_weight;
   const int64_t TT = tot >> kCountBits;
   const int64_t WT = TT + A * (tot & kCountMask);
-  const int64_t x0 = span_start(w, WT, a.num_parts, a.xcd_weighted);
-  const int64_t x1 = span_start(w + 1, WT, a.num_parts, a.xcd_weighted);
+  const int64_t x0 = dcp_span_start(w, WT, a.num_parts, a.xcd_weighted);
+  const int64_t x1 = dcp_span_start(w + 1, WT, a.num_parts, a.xcd_weighted);
   // Walk this thread's requests; the one whose weighted range holds x0 (x1) gives
   // the span's first (end) tile.
   int64_t F = excl >> kCountBits;
@@ -224,8 +183,8 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
       prefix_out[a.batch + 1 + b] = WP;
       int64_t span_range = 0;
       if (n > 0) {
-        const int64_t wf = span_of(WP + A, WT, a.num_parts, a.xcd_weighted);
-        const int64_t wl = span_of(WP + A + n - 1, WT, a.num_parts, a.xcd_weighted);
+        const int64_t wf = dcp_span_of(WP + A, WT, a.num_parts, a.xcd_weighted);
+        const int64_t wl = dcp_span_of(WP + A + n - 1, WT, a.num_parts, a.xcd_weighted);
         span_range = (wf << 32) | wl;
       }
       prefix_out[2 * a.batch + 2 + b] = span_range;
@@ -233,10 +192,10 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
     if (n > 0) {
       const int64_t wend = WP + A + n;
       if (x0 < x1 && WP <= x0 && x0 < wend) {
-        const int64_t off = x0 - WP - A > 0 ? x0 - WP - A : 0;
-        s_loc[0] = b; s_loc[1] = off; s_loc[2] = F + off;
+        const int64_t start = dcp_span_cut(x0, WP, A, F);
+        s_loc[0] = b; s_loc[1] = start - F; s_loc[2] = start;
       }
-      if (WP <= x1 && x1 < wend) s_loc[3] = F + (x1 - WP - A > 0 ? x1 - WP - A : 0);
+      if (WP <= x1 && x1 < wend) s_loc[3] = dcp_span_cut(x1, WP, A, F);
       F += n;
       WP = wend;
     }

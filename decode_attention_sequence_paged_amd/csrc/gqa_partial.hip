@@ -302,8 +302,9 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       const bool whole = piece_t0 == 0 && last_of_req;
       const int64_t slot = 2 * w + (first_piece ? 0 : 1);
       pend = true;
-      pend_inv = 1.0f / l_run;
-      pend_lse = (m_run + fast_log2(l_run)) * kLn2;
+      // a row that saw no token of the piece: O = 0, LSE = -inf
+      pend_inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+      pend_lse = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
       pend_o = (whole ? p.out_o + ((int64_t)cur.b * p.out_req_rows + head) * kD : p.ws_o + (slot * H + head) * kD) + 4 * q4;
       pend_l = whole ? p.out_lse + (int64_t)cur.b * p.out_req_rows + head : p.ws_lse + slot * H + head;
       piece_t0 = 0;

@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void rescale_kernel(const float* __restrict__ 
     const float g = lse[row], l = lse_r[row];
     // a rank without tokens (or a row nobody attended) carries no weight
     const float s = (g == -INFINITY || l == -INFINITY) ? 0.f : fast_exp2((l - g) * kLog2e);
-    const f32x4 v = ((const f32x4*)o)[e] * s;
+    // written as a select, so that a part without weight gives 0 even where its O holds NaN
+    const f32x4 v = s == 0.f ? f32x4{} : ((const f32x4*)o)[e] * s;
     if (BF16) {
       bf16x4 b;
 #pragma unroll

@@ -87,11 +87,9 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_r
     __syncthreads();  // the previous round's LDS reads are done
     for (int i = threadIdx.x; i < cnt; i += C::kThreads) {
       const int64_t w = base + i;
-      const int64_t x0 = span_start(w, WT, P, xw);
-      const bool empty = x0 == span_start(w + 1, WT, P, xw);  // an empty span holds no piece
-      // The first span may start before the request (it is that span's last piece);
-      // every later one starts inside it (its first piece).
-      const int64_t slot = empty ? -1 : 2 * w + (w == w_lo && x0 < WP ? 1 : 0);
+      const int64_t x0 = dcp_span_start(w, WT, P, xw);
+      // an empty span holds no piece
+      const int64_t slot = dcp_span_empty(w, WT, P, xw) ? -1 : dcp_piece_slot(w, w_lo, x0, WP);
       s_slot[i] = slot;
 #pragma unroll
       for (int h = 0; h < C::kHpb; ++h)
@@ -115,7 +113,7 @@ __global__ __launch_bounds__((SplitCfg<DV, PL, DS, QPT>::kThreads)) void split_r
           const int i = i0 + u * PL;
           const int64_t slot = i < cnt ? s_slot[i] : -1;
           // empty pieces (a causally masked row) carry no weight
-          const float l = s_lse[i][hd];
+          const float l = i < cnt ? s_lse[i][hd] : -INFINITY;
           wt[u] = slot >= 0 && l != -INFINITY ? fast_exp2(l - mx) : 0.f;
 #pragma unroll
           for (int k = 0; k < QPT; ++k)

@@ -81,7 +81,7 @@ typedef struct {
 } dcp_attn_desc_t;
 
 /* Human-readable name of a status code (static storage). */
-const char* dcp_status_string(int32_t status);
+const char* dcp_status_string(dcp_status_t status);
 
 /* ------------------------------------------------------------------ shard map
  * Blog Sec. 4 and Sec. 2.2; interleave size from the vLLM-Ascend guide.     */
