@@ -267,8 +267,7 @@ def run_next(args):
     for q_len in (1, 2, 4):
         qw = di.Workload(**dict(wl.__dict__, batch=B * q_len, lengths=tuple(wl.lengths) * q_len))
         q = paged.device_query(qw).view(B, q_len, H, Dqk)
-        ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(desc, q_len, B, 0), dtype=torch.uint8,
-                         device="cuda")
+        ws = paged.workspace_for(wl, 0, q_len=q_len)
         o = torch.empty((B, q_len, H, Dv), device="cuda")
         lse = torch.empty((B, q_len, H), device="cuda")
         t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl,
@@ -295,8 +294,7 @@ def run_next(args):
     for q_len in (1, 2, 4):
         qw = di.Workload(**dict(gw.__dict__, batch=GB * q_len, lengths=tuple(gw.lengths) * q_len))
         q = paged.device_query(qw).view(GB, q_len, GH, gw.qk_dim)
-        ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(gdesc, q_len, GB, 0), dtype=torch.uint8,
-                         device="cuda")
+        ws = paged.workspace_for(gw, 0, q_len=q_len)
         o = torch.empty((GB, q_len, GH, gw.v_dim), device="cuda")
         lse = torch.empty((GB, q_len, GH), device="cuda")
         t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(gdesc, q, grc.k_cache, grc.v_cache,

@@ -125,11 +125,14 @@ def desc_for(wl) -> "dcp.AttnDesc":
                          wl.softmax_scale)
 
 
-def workspace_for(wl, num_partitions: int = 0) -> torch.Tensor:
-    nbytes = dcp.dcp_decode_workspace_size(desc_for(wl), wl.batch, num_partitions)
+def workspace_for(wl, num_partitions: int = 0, q_len: int = 1) -> torch.Tensor:
+    """A zero-initialised workspace for the workload's partial calls."""
+    nbytes = dcp.dcp_decode_workspace_size_mtp(desc_for(wl), q_len, wl.batch, num_partitions)
     if nbytes == 0:
         raise ValueError("unsupported workload shape for %s" % wl.name)
-    return torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dcp.dcp_workspace_init(ws)
+    return ws
 
 
 def run_partial(wl, rc: RankCache, q: torch.Tensor, seq_lens_dev: torch.Tensor, out_o, out_lse,

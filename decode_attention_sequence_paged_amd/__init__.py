@@ -25,6 +25,9 @@ DCP_KV_MLA_LATENT = 0
 DCP_KV_GQA = 1
 DCP_DTYPE_F32 = 0
 DCP_DTYPE_BF16 = 1
+DCP_DEVERR_PAGE_ID = 1
+DCP_DEVERR_TABLE_SHORT = 2
+DCP_DEVERR_NEG_LENGTH = 4
 
 
 def _torch():
@@ -68,6 +71,8 @@ _SIGS = {
                                       _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "dcp_rescale_partial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "dcp_sum_head_slice": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "dcp_workspace_init": (_i32, [_vp, _sz, _vp]),
+    "dcp_workspace_errors": (_i32, [_vp, _sz, _vp, _i32, _vp]),
 }
 EXPORTED = tuple(_SIGS)
 
@@ -170,6 +175,21 @@ def dcp_local_block_table(global_block_table, num_ranks: int, interleave: int, b
     _check("dcp_local_block_table", lib().dcp_local_block_table(
         _dptr(global_block_table), B, mg, num_ranks, interleave, block_size, rank,
         _dptr(local_block_table), ml, _stream(stream)))
+
+
+def dcp_workspace_init(workspace, stream=None) -> None:
+    """Zero a partial-attention workspace (once, after allocation)."""
+    _check("dcp_workspace_init", lib().dcp_workspace_init(
+        _dptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dcp_workspace_errors(workspace, clear: bool = False, stream=None) -> int:
+    """The workspace's device error word (DCP_DEVERR_* bits); synchronises the stream."""
+    bits = ctypes.c_uint32(0)
+    _check("dcp_workspace_errors", lib().dcp_workspace_errors(
+        _dptr(workspace), workspace.numel() * workspace.element_size(), ctypes.addressof(bits),
+        1 if clear else 0, _stream(stream)))
+    return int(bits.value)
 
 
 def dcp_decode_workspace_size(desc: AttnDesc, batch: int, num_partitions: int = 0) -> int:

@@ -66,6 +66,18 @@ dcp_status_t check_desc(const dcp_attn_desc_t* d, int32_t* head_groups) {
   return DCP_ERROR_INVALID_VALUE;
 }
 
+}  // namespace
+
+namespace dcp {
+// Head-group policies (host side; the kernels' launchers use them too).
+int mla_heads_per_group(int num_q_heads) { return num_q_heads <= 32 ? 32 : 64; }
+int gqa_kv_heads_per_group(int num_kv_heads) {
+  return num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
+}
+}  // namespace dcp
+
+namespace {
+
 // Tiles of work charged to each request a work-group touches (see the partition
 // helpers in dcp_device.h): the query slice it reads and the fp32 output row it
 // writes, in units of the tile bytes it streams.  MLA: a 64-head group moves 72 KiB
@@ -84,13 +96,18 @@ int32_t default_parts(int32_t head_groups) {
   return p < 1 ? 1 : p;
 }
 
+// Workspace of a partial call: a 256-byte header (the device error word at offset 0),
+// the per-slot and per-request arrival counters of the in-kernel split-K merge, the
+// partition prefix, and the split pieces' LSEs and outputs.  dcp_workspace_init zeroes
+// it once; the kernels leave the counters at zero after every call.
 struct WsLayout {
-  size_t prefix, lse, o, total;
+  size_t cnt, prefix, lse, o, total;
 };
 
 WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   WsLayout l;
-  l.prefix = 256;
+  l.cnt = 256;
+  l.prefix = l.cnt + align256(sizeof(uint32_t) * (2 * (size_t)parts + (size_t)batch));
   l.lse = l.prefix + align256(sizeof(int64_t) * (3 * (size_t)batch + 2));
   l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
   l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);
@@ -132,6 +149,27 @@ const char* dcp_status_string(dcp_status_t status) {
     case DCP_ERROR_HIP: return "DCP_ERROR_HIP";
     default: return "DCP_ERROR_UNKNOWN";
   }
+}
+
+dcp_status_t dcp_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes == 0 || ((uintptr_t)workspace & 255)) return DCP_ERROR_INVALID_VALUE;
+  return hip_status(dcp::launch_zero_fill(workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+dcp_status_t dcp_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* error_bits,
+                                  int32_t clear, void* stream) {
+  if (!workspace || !error_bits || workspace_bytes < 256) return DCP_ERROR_INVALID_VALUE;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t word = 0;
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return DCP_ERROR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DCP_ERROR_HIP;
+  *error_bits = word;
+  if (clear) {
+    if (dcp::launch_zero_fill((void*)workspace, sizeof(uint32_t), s) != hipSuccess) return DCP_ERROR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return DCP_ERROR_HIP;
+  }
+  return DCP_SUCCESS;
 }
 
 dcp_status_t dcp_shard_map(const int32_t* seq_lens, int32_t batch, int32_t num_ranks,
@@ -286,6 +324,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   p.out_lse = out_lse;
   p.q_req_stride = (int64_t)d.num_q_heads * d.qk_dim;
   p.out_req_rows = d.num_q_heads;
+  p.ws_err = (uint32_t*)ws;
   p.ws_prefix = (int64_t*)(ws + wl.prefix);
   p.ws_lse = (float*)(ws + wl.lse);
   p.ws_o = (float*)(ws + wl.o);

@@ -99,6 +99,22 @@ __device__ __forceinline__ T ld_const(const T* ptr) {
   return *(const __attribute__((address_space(4))) T*)ptr;
 }
 
+// Page id of a block-table entry, clamped into the pool (an entry outside [0, num_blocks)
+// reads page 0, so no copy leaves the pool); such an entry sets `bad`.
+__device__ __forceinline__ int32_t checked_page(int32_t page, int64_t num_blocks, bool& bad) {
+  const bool out = page < 0 || (int64_t)page >= num_blocks;
+  bad = bad || out;
+  return out ? 0 : page;
+}
+
+// Bit values of the device error word (the same as dcp_device_error_t in dcp.h).
+constexpr uint32_t kErrPageId = 1u, kErrTableShort = 2u, kErrNegLength = 4u;
+
+// Adds bits to the device error word (one lane of a wave calls it; vector atomic).
+__device__ __forceinline__ void report_error(uint32_t* err, uint32_t bits) {
+  __hip_atomic_fetch_or(err, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ work partitions
 //
 // How a rank's tiles are cut into spans of equal work, and which workspace slot each
@@ -131,11 +147,12 @@ struct SpanLoc {
 // (prefix_out[b], the total at prefix_out[B]), weighted position (prefix_out[B + 1 +
 // b], the weighted total at prefix_out[2 B + 1]) and the spans of its first and last
 // tiles (prefix_out[2 B + 2 + b] = w_first << 32 | w_last; 0 for a request without
-// tiles), so that the split reduce need not repeat the partition arithmetic.  s_scan must hold blockDim.x / 64
+// tiles), so that the split reduce need not repeat the partition arithmetic, and adds to
+// *err_word the bits of the lengths it had to clamp.  s_scan must hold blockDim.x / 64
 // int64 values; s_loc four int64 values.
 template <int NT>
 __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
-                               int64_t* s_scan, int64_t* s_loc) {
+                               uint32_t* err_word, int64_t* s_scan, int64_t* s_loc) {
   constexpr int64_t kCountMask = (int64_t(1) << kCountBits) - 1;
   const int tid = threadIdx.x;
   const int per = (a.batch + NT - 1) / NT;
@@ -176,9 +193,15 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
   // the span's first (end) tile.
   int64_t F = excl >> kCountBits;
   int64_t WP = F + A * (excl & kCountMask);
+  uint32_t err = 0;
   for (int b = b_lo; b < b_hi; ++b) {
     const int64_t n = part_tiles(a, b);
     if (prefix_out) {
+      // device-resident lengths the kernels had to clamp (checked by one work-group)
+      const int32_t raw = ld_const(a.seq_lens + b);
+      if (raw < 0) err |= kErrNegLength;
+      const int64_t Lr = dcp_local_len(raw - (int64_t)a.len_offset, a.num_ranks, a.interleave, a.rank);
+      if (Lr > (int64_t)a.max_blocks_per_seq * a.block_size) err |= kErrTableShort;
       prefix_out[b] = F;
       prefix_out[a.batch + 1 + b] = WP;
       int64_t span_range = 0;
@@ -201,6 +224,7 @@ __device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefi
     }
   }
   if (prefix_out && tid == NT - 1) { prefix_out[a.batch] = TT; prefix_out[2 * a.batch + 1] = WT; }
+  if (err) report_error(err_word, err);
   __syncthreads();
   // Every lane read the same LDS values; say so, so that what the kernels derive from
   // the span (loop bounds, page bases) stays in scalar registers.
@@ -234,9 +258,6 @@ __device__ __forceinline__ void block_to_span(int num_parts, int num_groups, int
   }
 }
 
-__device__ __forceinline__ int32_t clamp_page(int32_t page, int64_t num_blocks) {
-  return (page < 0 || (int64_t)page >= num_blocks) ? 0 : page;
-}
 
 
 constexpr int kTileTokens = 32;  // tokens per streamed tile (both kernels)

@@ -30,6 +30,7 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int32_t nu
                         int32_t v_dim, float* out_o, float* out_lse, hipStream_t stream);
 hipError_t launch_shard_map(const int32_t* seq_lens, int32_t batch, int32_t N, int32_t I,
                             int32_t rank, int32_t* local_lens, hipStream_t stream);
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_local_block_table(const int32_t* gbt, int32_t batch, int32_t max_global, int32_t N,
                                     int32_t P, int32_t rank, int32_t* lbt, int32_t max_local,
                                     hipStream_t stream);

@@ -36,6 +36,7 @@ struct PartialParams {
   int64_t q_req_stride;     // GQA: query elements between consecutive requests (H * qk_dim unless a
                             // query token of a multi-token batch)
   int64_t out_req_rows;     // GQA: output rows between consecutive requests (H unless likewise)
+  uint32_t* ws_err;         // device error word (dcp_device_error_t bits)
   int64_t* ws_prefix;       // [3 B + 2]: tile prefix, weighted prefix, span range of each request
   float* ws_lse;            // [2P, H]
   float* ws_o;              // [2P, H, v_dim]

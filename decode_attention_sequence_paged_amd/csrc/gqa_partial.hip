@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   block_to_span(p.part.num_parts, p.num_head_groups, &w, &hg);
   const bool write_prefix = (w == 0 && hg == 0);
   const SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
-                                               s_scan, s_loc);
+                                               p.ws_err, s_scan, s_loc);
   if (loc.start >= loc.end) return;
   const int total = (int)(loc.end - loc.start);
   const int bs = p.block_size;
@@ -142,8 +142,9 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   // into a stage no wave reads.
   int lc_left = total;
   int64_t src = 0;
+  bool bad_page = false;
   auto next_src = [&]() {
-    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    const int32_t page = checked_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks, bad_page);
     src = uniform64(page * page_bytes + (int64_t)lc.sub * kTile * row_stride);
   };
   auto advance_loader = [&]() {
@@ -315,15 +316,12 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     advance_loader();
   }
   flush_piece();
+  if (bad_page && lane == 0) report_error(p.ws_err, kErrPageId);
   // No copy may still be landing in this work-group's LDS when it exits.
   wait_vmcnt_builtin<0>();
 }
 
 }  // namespace gqa
-
-int gqa_kv_heads_per_group(int num_kv_heads) {
-  return num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
-}
 
 hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   block_to_span(p.part.num_parts, p.num_head_groups, &w, &hg);
   const bool write_prefix = (w == 0 && hg == 0);
   const SpanLoc loc = locate_span<C::kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
-                                               s_scan, s_loc);
+                                               p.ws_err, s_scan, s_loc);
   if (loc.start >= loc.end) return;
   const int total = (int)(loc.end - loc.start);
   const int tpp = p.block_size / kTile;                    // tiles per page
@@ -178,8 +178,9 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   // reads) so that the copy code in the loop needs no branch.
   int lc_left = total;  // tiles the loader has not moved past yet
   const uint8_t* src = nullptr;
+  bool bad_page = false;
   auto next_src = [&]() {
-    const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+    const int32_t page = checked_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks, bad_page);
     src = p.k_cache + page * page_bytes + lc.sub * kTileBytes;
   };
   auto advance_loader = [&]() {
@@ -440,6 +441,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     advance_loader();
   }
   flush_piece();
+  if (bad_page && lane == 0) report_error(p.ws_err, kErrPageId);
   // No copy may still be landing in this work-group's LDS when it exits.
   wait_vmcnt_builtin<0>();
 }
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
   const bool write_prefix = (w == 0 && hg == 0);
   // The span scan's scratch lives in the first stage, before any copy lands there.
   const SpanLoc loc = locate_span<kThreads>(p.part, w, write_prefix ? p.ws_prefix : nullptr,
-                                            (int64_t*)smem, s_loc);
+                                            p.ws_err, (int64_t*)smem, s_loc);
   if (loc.start >= loc.end) return;
   const int total = (int)(loc.end - loc.start);
   const int tpp = p.block_size / kTile;
@@ -687,8 +689,9 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
     Cursor lc = cur0;
     int lc_left = total;
     const uint8_t* src = nullptr;
+    bool bad_page = false;
     auto next_src = [&]() {
-      const int32_t page = clamp_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks);
+      const int32_t page = checked_page(ld_const(lc.bt_row + lc.pk), p.num_cache_blocks, bad_page);
       src = p.k_cache + page * page_bytes + lc.sub * kTileBytes;
     };
     auto issue_tile = [&](int stage) {
@@ -799,14 +802,13 @@ __global__ __launch_bounds__(wide::kThreads, 1) void mla_partial_wide_kernel(Par
       }
     }
     flush_piece();
+    if (bad_page && lane == 0) report_error(p.ws_err, kErrPageId);
     // No copy may still be landing in this work-group's LDS when it exits.
     wait_vmcnt_builtin<0>();
   }
 }
 
 }  // namespace mla
-
-int mla_heads_per_group(int num_q_heads) { return num_q_heads <= 32 ? 32 : 64; }
 
 hipError_t launch_mla_partial(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;

@@ -248,6 +248,25 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int32_t nu
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ workspace fill
+// Zeroes `bytes` bytes (16 per thread, the tail byte-wise); a kernel rather than a
+// memset so that the call can sit in a captured graph.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint8_t* __restrict__ p, size_t bytes) {
+  const size_t quads = bytes / 16;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < quads; i += (size_t)gridDim.x * blockDim.x)
+    ((u32x4*)p)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (blockIdx.x == 0 && threadIdx.x < bytes - quads * 16) p[quads * 16 + threadIdx.x] = 0;
+}
+
+hipError_t launch_zero_fill(void* ptr, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return hipSuccess;
+  size_t blocks = (bytes / 16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t*)ptr, bytes);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ shard map kernels
 __global__ void shard_map_kernel(const int32_t* __restrict__ seq_lens, int32_t batch, int32_t N,
                                  int32_t I, int32_t rank, int32_t* __restrict__ local_lens) {

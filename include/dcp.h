@@ -38,9 +38,12 @@
  *               and nothing runs.  DCP_ERROR_HIP reports a failed launch.
  *               Device-resident values the host cannot see (page ids, lengths)
  *               are clamped by the kernels so that no access leaves its buffer:
- *               out-of-range page ids are replaced by page 0, negative lengths read
- *               as 0, and a rank never reads more than max_blocks_per_seq pages of
- *               a request.  Such inputs give meaningless numbers, never a fault.
+ *               a block-table entry outside [0, num_cache_blocks) is read as page
+ *               0, a negative seq_lens entry as 0, and a rank never reads more than
+ *               max_blocks_per_seq pages of a request.  Such inputs give
+ *               meaningless numbers, never a fault; the partial-attention calls
+ *               also record each such event as a bit of the workspace's device
+ *               error word (dcp_workspace_errors below).
  */
 #ifndef DCP_H_
 #define DCP_H_
@@ -133,6 +136,28 @@ dcp_status_t dcp_local_block_table(const int32_t* global_block_table, int32_t ba
 /* ------------------------------------------------------------------ partial attention
  * Blog Sec. 4.1 "Compute", Sec. 5.3 (MLA), Sec. 5.4 (GQA).                 */
 
+/* Device error word of a workspace: bits the partial-attention kernels set when they
+ * clamp a device-resident value (see "Errors" above).  The bits accumulate over calls
+ * until cleared. */
+typedef enum {
+  DCP_DEVERR_PAGE_ID = 1u,     /* a block-table entry outside [0, num_cache_blocks) was read */
+  DCP_DEVERR_TABLE_SHORT = 2u, /* a request's local length exceeded max_blocks_per_seq pages */
+  DCP_DEVERR_NEG_LENGTH = 4u   /* a seq_lens entry was negative */
+} dcp_device_error_t;
+
+/* Zero a workspace for dcp_decode_partial / dcp_decode_partial_mtp (device; enqueued
+ * on `stream`, no allocation).  Needed once after allocation; the calls keep the
+ * workspace's counters at zero themselves.
+ * Errors: INVALID_VALUE for a NULL or misaligned workspace or zero bytes; HIP. */
+dcp_status_t dcp_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Read the device error word of a workspace into *error_bits (host), after the work
+ * enqueued on `stream` so far; clears the word if `clear` is nonzero.  Synchronises
+ * `stream` (a diagnostic, not for the decode loop).
+ * Errors: INVALID_VALUE for NULL pointers or a workspace smaller than 256 bytes; HIP. */
+dcp_status_t dcp_workspace_errors(const void* workspace, size_t workspace_bytes, uint32_t* error_bits,
+                                  int32_t clear, void* stream);
+
 /* Workspace bytes dcp_decode_partial needs for `batch` requests split into
  * `num_partitions` token-balanced work partitions (0 = the library's default
  * for the current device).  Returns 0 for an invalid or unsupported desc.     */
@@ -160,7 +185,11 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *                request cut between partitions is reduced in a second kernel
  *                (split-K).
  *   workspace    device, >= dcp_decode_workspace_size(desc, batch, num_partitions)
- *                bytes, 256-byte aligned; contents need no initialisation.
+ *                bytes, 256-byte aligned, zeroed once by dcp_workspace_init before its
+ *                first use (it holds counters the kernels leave at zero after every
+ *                call, and the device error word).  Calls that share a workspace
+ *                must be ordered (one stream); a workspace is not shared between
+ *                calls that may run concurrently.
  *   out_o        device fp32 [batch, H, v_dim], written: normalised partial output
  *                O_r = sum_t p_t v_t / sum_t p_t over the rank's tokens.
  *   out_lse      device fp32 [batch, H], written: LSE_r = ln sum_t exp(s_t),

@@ -59,6 +59,14 @@ int main(void) {
   check(dcp_merge((const float*)f, (const float*)f, 0, 2, 4, 512, (float*)f, (float*)f, NULL) ==
             DCP_ERROR_INVALID_VALUE,
         "merge: zero parts rejected");
+  check(dcp_workspace_init(NULL, 4096, NULL) == DCP_ERROR_INVALID_VALUE, "workspace_init: NULL rejected");
+  check(dcp_workspace_init((char*)f + 4, 4096, NULL) == DCP_ERROR_INVALID_VALUE,
+        "workspace_init: misaligned workspace rejected");
+  uint32_t bits = 0;
+  check(dcp_workspace_errors(f, 128, &bits, 0, NULL) == DCP_ERROR_INVALID_VALUE,
+        "workspace_errors: short workspace rejected");
+  check(dcp_workspace_errors(f, 4096, NULL, 0, NULL) == DCP_ERROR_INVALID_VALUE,
+        "workspace_errors: NULL output rejected");
   printf("%d failures\n", failures);
   return failures != 0;
 }

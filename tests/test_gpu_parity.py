@@ -538,7 +538,7 @@ def run_rank_mtp(wl, rank, q_len, census=False, parts=0):
     q = pg.device_query(qw, census=census).view(B, q_len, H, wl.qk_dim)
     sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
     desc = pg.desc_for(wl)
-    ws = torch.empty(dcp.dcp_decode_workspace_size_mtp(desc, q_len, B, parts), dtype=torch.uint8, device="cuda")
+    ws = pg.workspace_for(wl, parts, q_len=q_len)
     o = torch.full((B, q_len, H, wl.v_dim), float("nan"), device="cuda")
     lse = torch.full((B, q_len, H), float("nan"), device="cuda")
     dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, rc.v_cache, rc.block_table, sl, rank, wl.dcp_size,
