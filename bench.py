@@ -50,13 +50,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_traffic.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mla_long_b128")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: mla_c512; with --next: mla_long_b128)")
     ap.add_argument("--partitions", type=int, default=0, help="work partitions per head group (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=10.0,
-                    help="seconds of oracle math to time for the CPU baseline")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other workloads' figures (per_config)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of host work (oracle math + input regeneration) for the CPU baseline")
     ap.add_argument("--bands", action="store_true",
                     help="rank-0 partial bandwidth per request-length band instead of the step")
     ap.add_argument("--next", action="store_true",
@@ -66,6 +69,12 @@ def parse():
                     help="before timing, run one plain device-to-device copy of this many bytes "
                          "(a reference for scaling the HBM byte counters of a profiler run)")
     return ap.parse_args()
+
+
+def single_kernel_call(wl) -> bool:
+    """Whether a partial call of this workload is one kernel launch (requests split between
+    work partitions merged inside the kernel) or two (a split-K reduce kernel follows)."""
+    return False
 
 
 def describe(wl) -> str:
@@ -105,10 +114,10 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(wl, budget_s: float):
-    """Time the float64 oracle on the host: per-rank partial attention of the
-    workload's requests, rank 0 first, then rank 1, ... until about ``budget_s``
-    seconds of attention math have been timed (input regeneration is timed
-    separately and excluded)."""
+    """Time the float64 oracle on the host: per-rank partial attention of the workload's
+    requests, rank 0's requests in batch order, then rank 1's, ..., until about
+    ``budget_s`` seconds of host work (attention math plus input regeneration) are spent.
+    Only the attention math is timed for the rate."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -117,8 +126,9 @@ def cpu_baseline(wl, budget_s: float):
         threads = len(os.sched_getaffinity(0))
     tokens = 0
     t_math = t_gen = 0.0
-    done = []
+    done = []  # (rank, requests)
     for r in range(wl.dcp_size):
+        n_req = 0
         for b in range(wl.batch):
             toks = oracle.rank_tokens(int(wl.lengths[b]), wl.dcp_size, wl.interleave, r)
             t0 = time.perf_counter()
@@ -129,20 +139,23 @@ def cpu_baseline(wl, budget_s: float):
             t_gen += t1 - t0
             t_math += t2 - t1
             tokens += toks.size
+            n_req += 1
             del q, K, V
-        done.append(r)
-        if t_math >= budget_s:
+            if t_math + t_gen >= budget_s:
+                break
+        done.append((r, n_req))
+        if t_math + t_gen >= budget_s:
             break
     kv_bytes = tokens * (wl.qk_dim * 2 if wl.kind == "mla" else wl.num_kv_heads * (wl.qk_dim + wl.v_dim) * 2)
+    sample = "; ".join("rank %d: requests 0..%d of %d" % (r, n - 1, wl.batch) for r, n in done)
     return {
         "value": round(kv_bytes / t_math / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": "per-rank partial attention of all %d requests on ranks %s of %d (%d local tokens); "
-                  "%.3g s of float64 math timed, input regeneration (%.3g s) excluded; "
-                  "rate in bf16-KV bytes per second"
-                  % (wl.batch, ",".join(map(str, done)), wl.dcp_size, tokens, t_math, t_gen),
+        "sample": "per-rank partial attention (float64 numpy, %d BLAS threads) of %s (%d local tokens); "
+                  "%.3g s of attention math timed, input regeneration (%.3g s) excluded; rate in "
+                  "bf16-KV bytes per second" % (threads, sample, tokens, t_math, t_gen),
         "tokens_per_s": round(tokens / t_math, 1),
     }
 
@@ -249,7 +262,7 @@ def run_next(args):
 
     dcp.lib()
     torch.cuda.set_device(0)
-    wl = di.WORKLOADS[args.workload]
+    wl = di.WORKLOADS[args.workload or "mla_long_b128"]
     if wl.kind != "mla":
         raise SystemExit("--next runs on an MLA workload")
     N, B, H, Dqk, Dv, bs = wl.dcp_size, wl.batch, wl.num_q_heads, wl.qk_dim, wl.v_dim, wl.block_size
@@ -352,6 +365,157 @@ def run_next(args):
     print(json.dumps(out), flush=True)
 
 
+class Group:
+    """Every rank's page pool of one workload, resident in HBM, and the buffers of a
+    step: the N ranks' partial calls (one after another on this GPU) and the N-way merge."""
+
+    def __init__(self, wl, partitions: int = 0):
+        import torch
+        import decode_attention_sequence_paged_amd as dcp
+        from dcp_inputs import paged
+        self.wl, self.partitions, self.dcp, self.paged = wl, partitions, dcp, paged
+        N, B, H = wl.dcp_size, wl.batch, wl.num_q_heads
+        self.q = paged.device_query(wl)
+        self.sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+        self.ranks = [paged.build_rank_cache(wl, r) for r in range(N)]
+        self.ws = paged.workspace_for(wl, partitions)
+        self.o_all = torch.empty((N, B, H, wl.v_dim), device="cuda")
+        self.l_all = torch.empty((N, B, H), device="cuda")
+        self.o = torch.empty((B, H, wl.v_dim), device="cuda")
+        self.lse = torch.empty((B, H), device="cuda")
+        torch.cuda.synchronize()
+        Dqk, Dv = wl.qk_dim, wl.v_dim
+        # KV bytes per local token: MLA one 576-dim latent row serving as K and V; GQA a K
+        # and a V row per KV head.
+        row = Dqk * 2 if wl.kind == "mla" else wl.num_kv_heads * (Dqk + Dv) * 2
+        self.local = np.array([rc.total_local for rc in self.ranks], dtype=np.float64)
+        pages = np.array([int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum())
+                          for rc in self.ranks])
+        self.kv_bytes = self.local * row
+        # compulsory bytes of one partial call: KV rows once, q, O_r, LSE_r, block-table entries
+        self.call_bytes = self.kv_bytes + B * H * (Dqk * 2 + Dv * 4 + 4) + pages * 4
+        self.merge_bytes = (N + 1) * B * H * (Dv + 1) * 4
+        self.flops = 2.0 * H * (Dqk + Dv) * self.local
+
+    def step(self, evs=None):
+        """One step; with evs, a pair of HIP events (on the launch stream) around each of the
+        N partial calls and the merge."""
+        N = self.wl.dcp_size
+        for r in range(N):
+            if evs is not None:
+                evs[r][0].record()
+            self.paged.run_partial(self.wl, self.ranks[r], self.q, self.sl, self.o_all[r], self.l_all[r],
+                                   self.ws, self.partitions)
+            if evs is not None:
+                evs[r][1].record()
+        if evs is not None:
+            evs[N][0].record()
+        self.dcp.dcp_merge(self.o_all, self.l_all, self.o, self.lse)
+        if evs is not None:
+            evs[N][1].record()
+
+    def events(self, steps):
+        import torch
+        return [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(self.wl.dcp_size + 1)] for _ in range(steps)]
+
+    def timed(self, steps: int, warmup: int, flush=None):
+        """Warm-up, then `steps` steps with events around every call, bracketed by
+        synchronize; no synchronisation between the steps.  With `flush` (a >= 1 GiB device
+        buffer), each step is preceded by a write of the whole buffer, outside the events
+        (the wall time then includes the flushes).  Returns (wall seconds, per-call ms
+        [steps, N + 1])."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = self.events(steps)
+        t0 = time.perf_counter()
+        for s in range(steps):
+            if flush is not None:
+                flush.zero_()
+            self.step(evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, np.array([[a.elapsed_time(b) for a, b in e] for e in evs])
+
+    def summary(self, wall: float, per_call: np.ndarray) -> dict:
+        """Figures of one timed pass (call durations: median / p10 / p90 over the steps,
+        and the mean the roofline uses)."""
+        N, steps = self.wl.dcp_size, per_call.shape[0]
+        calls = per_call[:, :N]
+        t_rank_mean = calls.mean(axis=0)
+        t_merge = float(per_call[:, N].mean())
+        ms_per_step = wall * 1e3 / steps
+        achieved = float(self.call_bytes.mean() / (t_rank_mean.mean() * 1e-3) / 1e9)
+        pct = lambda a, q: round(float(np.percentile(a, q)), 4)
+        step_event_ms = float(per_call.sum(axis=1).mean())
+        return {
+            "ms_per_step": round(ms_per_step, 4),
+            "kv_gbps": round(float(self.kv_bytes.sum() / (ms_per_step * 1e-3) / 1e9), 2),
+            "step_event_ms": round(step_event_ms, 4),
+            "rank_call_ms_median": [pct(calls[:, r], 50) for r in range(N)],
+            "rank_call_ms_p10": [pct(calls[:, r], 10) for r in range(N)],
+            "rank_call_ms_p90": [pct(calls[:, r], 90) for r in range(N)],
+            "rank_call_ms_mean": [round(float(x), 4) for x in t_rank_mean],
+            "call_ms_median_all_ranks": pct(calls, 50),
+            "call_ms_p10_all_ranks": pct(calls, 10),
+            "call_ms_p90_all_ranks": pct(calls, 90),
+            "merge_ms_median": pct(per_call[:, N], 50),
+            "merge_ms_mean": round(t_merge, 4),
+            "merge_frac": round(t_merge / step_event_ms, 4),
+            "merge_gbps": round(self.merge_bytes / (t_merge * 1e-3) / 1e9, 1),
+            "call_achieved_gbps": round(achieved, 2),
+            "call_frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "rank0_kv_gbps_median": round(float(self.kv_bytes[0] / (np.median(calls[:, 0]) * 1e-3) / 1e9), 2),
+            "mfma_pct_bf16_peak": round(100.0 * float(self.flops.mean() / (t_rank_mean.mean() * 1e-3))
+                                        / (MFMA_BF16_PEAK_TFLOPS * 1e12), 2),
+        }
+
+    def free(self):
+        import torch
+        del self.ranks, self.q, self.ws, self.o_all, self.l_all, self.o, self.lse
+        torch.cuda.empty_cache()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def single_thread_tiny_oracle():
+    """The float64 oracle on one host thread: every rank's partials of the tiny MLA batch
+    (B=2, 16 heads, lengths 1000 and 3000, N=2, I=1), math only."""
+    import dcp_inputs as di
+    import oracle
+    from threadpoolctl import threadpool_limits
+    wl = di.WORKLOADS["mla_tiny"]
+    t_math, tokens = 0.0, 0
+    with threadpool_limits(limits=1):
+        for _ in range(5):
+            for r in range(wl.dcp_size):
+                for b in range(wl.batch):
+                    toks = oracle.rank_tokens(int(wl.lengths[b]), wl.dcp_size, wl.interleave, r)
+                    q, K, V = oracle.request_inputs(wl, b, toks)
+                    t0 = time.perf_counter()
+                    oracle.attention(q, K, V, wl.softmax_scale)
+                    t_math += time.perf_counter() - t0
+                    tokens += toks.size
+    return {"workload": "mla_tiny (B=2, 16 heads, N=2, I=1), every rank's partials, 5 repetitions",
+            "threads": 1, "seconds": round(t_math, 4), "tokens_per_s": round(tokens / t_math, 1),
+            "gbps": round(tokens * wl.qk_dim * 2 / t_math / 1e9, 4)}
+
+
+PER_CONFIG = ("gqa_b32", "mla_long_b128", "mla_1m")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -370,35 +534,13 @@ def main():
     import torch
     import dcp_inputs as di
     import decode_attention_sequence_paged_amd as dcp
-    from dcp_inputs import paged
 
     dcp.lib()
     torch.cuda.set_device(0)
-    wl = di.WORKLOADS[args.workload]
+    wl = di.WORKLOADS[args.workload or "mla_c512"]
     N = wl.dcp_size
-
-    q = paged.device_query(wl)
-    sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
-    ranks = [paged.build_rank_cache(wl, r) for r in range(N)]
-    ws = paged.workspace_for(wl, args.partitions)
-    o_all = torch.empty((N, wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
-    l_all = torch.empty((N, wl.batch, wl.num_q_heads), device="cuda")
-    o = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
-    lse = torch.empty((wl.batch, wl.num_q_heads), device="cuda")
-    torch.cuda.synchronize()
-
-    def step(evs=None):
-        for r in range(N):
-            if evs is not None:
-                evs[r][0].record()
-            paged.run_partial(wl, ranks[r], q, sl, o_all[r], l_all[r], ws, args.partitions)
-            if evs is not None:
-                evs[r][1].record()
-        if evs is not None:
-            evs[N][0].record()
-        dcp.dcp_merge(o_all, l_all, o, lse)
-        if evs is not None:
-            evs[N][1].record()
+    print("bench: building %s" % wl.name, file=sys.stderr, flush=True)
+    g = Group(wl, args.partitions)
 
     if args.copy_probe_bytes:
         src = torch.empty(args.copy_probe_bytes, dtype=torch.uint8, device="cuda")
@@ -407,47 +549,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps, bracketed by synchronize
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    # per-call durations with HIP events on the launch stream (separate pass)
-    per_call = np.zeros((args.steps, N + 1))
-    for s in range(args.steps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(N + 1)]
-        step(evs)
-        torch.cuda.synchronize()
-        per_call[s] = [a.elapsed_time(b) for a, b in evs]
-    t_rank = per_call[:, :N].mean(axis=0)          # ms per rank call
-    t_merge = float(per_call[:, N].mean())
-
-    H, Dqk, Dv = wl.num_q_heads, wl.qk_dim, wl.v_dim
-    # KV bytes per local token: MLA one 576-dim latent row serving as K and V; GQA a K
-    # and a V row per KV head.
-    row_bytes = Dqk * 2 if wl.kind == "mla" else wl.num_kv_heads * (Dqk + Dv) * 2
-    local = np.array([rc.total_local for rc in ranks], dtype=np.float64)
-    pages = np.array([int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum()) for rc in ranks])
-    kv_bytes = local * row_bytes
-    # compulsory bytes of one partial call: KV rows once, q, O_r, LSE_r, block-table entries
-    call_bytes = kv_bytes + wl.batch * H * (Dqk * 2 + Dv * 4 + 4) + pages * 4
-    merge_bytes = (N + 1) * wl.batch * H * (Dv + 1) * 4
-    flops_rank = 2.0 * H * (Dqk + Dv) * local
-
-    achieved = float(call_bytes.mean() / (t_rank.mean() * 1e-3) / 1e9)
-    rank0_kv = float(kv_bytes[0] / (t_rank[0] * 1e-3) / 1e9)
-    value = float(kv_bytes.sum() / (ms_per_step * 1e-3) / 1e9)
-    step_event_ms = float(t_rank.sum() + t_merge)
-    traffic = measured_traffic(wl.name)
-
+    # timed region: exactly K steps bracketed by synchronize, HIP events around every call
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    wall, per_call = g.timed(args.steps, args.warmup)
+    warm = g.summary(wall, per_call)
+    # the same steps with a 1 GiB scratch write before each (caches flushed: cold)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    wall_c, per_call_c = g.timed(args.steps, 1, flush=flush)
+    cold = g.summary(wall_c, per_call_c)
+    del flush
+    ms_per_step = warm["ms_per_step"]
+    t_rank = np.array(warm["rank_call_ms_mean"])
+    achieved = warm["call_achieved_gbps"]
+    value = float(g.kv_bytes.sum() / (ms_per_step * 1e-3) / 1e9)
+    kernel_desc = ("dcp_decode_partial: %s partial kernel%s, mean over the %d ranks' calls"
+                   % (wl.kind, "" if single_kernel_call(wl) else " + split_reduce_kernel", N))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -470,35 +586,67 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "steps_per_s": round(1e3 / ms_per_step, 3),
         "decode_tokens_per_s": round(wl.batch * 1e3 / ms_per_step, 1),
-        "steps_per_s_per_rank_equiv": round(1e3 / (t_rank[0] + t_merge / N), 3),
-        "rank0_kv_gbps": round(rank0_kv, 2),
-        "rank0_pct_hbm_peak": round(100.0 * rank0_kv / HBM_PEAK_GBPS, 2),
-        "rank0_local_kv_tokens_per_s": round(local[0] / (t_rank[0] * 1e-3), 1),
-        "rank_call_ms": [round(float(x), 4) for x in t_rank],
-        "merge_ms": round(t_merge, 4),
-        "merge_frac": round(t_merge / step_event_ms, 4),
-        "merge_gbps": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
-        "mfma_pct_bf16_peak": round(100.0 * float(flops_rank.mean() / (t_rank.mean() * 1e-3))
-                                    / (MFMA_BF16_PEAK_TFLOPS * 1e12), 2),
+        "steps_per_s_per_rank_equiv": round(1e3 / (t_rank[0] + warm["merge_ms_mean"] / N), 3),
+        "rank0_kv_gbps": warm["rank0_kv_gbps_median"],
+        "rank0_pct_hbm_peak": round(100.0 * warm["rank0_kv_gbps_median"] / HBM_PEAK_GBPS, 2),
+        "rank0_local_kv_tokens_per_s": round(g.local[0] / (warm["rank_call_ms_median"][0] * 1e-3), 1),
+        "merge_frac": warm["merge_frac"],
+        "mfma_pct_bf16_peak": warm["mfma_pct_bf16_peak"],
+        "timing": {"timed_region": warm, "cold_1GiB_flush_before_each_step": cold,
+                   "note": "events around every call inside the timed region, no synchronisation "
+                           "between steps; call times median/p10/p90 over the steps"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "dcp_decode_partial (%s partial kernel + split_reduce_kernel), mean over ranks" % wl.kind,
-            "achieved": round(achieved, 2),
+            "kernel": kernel_desc,
+            "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "bytes_per_launch": round(float(call_bytes.mean())),
+            "traffic": measured_traffic(wl.name),
+            "bytes_per_launch": round(float(g.call_bytes.mean())),
             "launch_ms": round(float(t_rank.mean()), 4),
+            "cold_frac": cold["call_frac"],
         },
     }
-    del ranks
+    g.free()
+    del g
     torch.cuda.empty_cache()
+
+    # the other workloads: every rank's call and the merge, same protocol (timed region)
+    per_config = {}
+    if not args.no_per_config:
+        for name in PER_CONFIG:
+            if name == wl.name:
+                continue
+            print("bench: per-config %s" % name, file=sys.stderr, flush=True)
+            cw = di.WORKLOADS[name]
+            cg = Group(cw)
+            wall_x, pc_x = cg.timed(args.steps, args.warmup)
+            sx = cg.summary(wall_x, pc_x)
+            per_config[name] = {
+                "workload": describe(cw),
+                "calls": "partial kernel%s" % ("" if single_kernel_call(cw) else " + split_reduce_kernel"),
+                "call_frac": sx["call_frac"], "call_ms_median": sx["call_ms_median_all_ranks"],
+                "call_ms_p10": sx["call_ms_p10_all_ranks"], "call_ms_p90": sx["call_ms_p90_all_ranks"],
+                "rank_call_ms_median": sx["rank_call_ms_median"],
+                "ms_per_step": sx["ms_per_step"], "kv_gbps": sx["kv_gbps"],
+                "pct_hbm_peak": round(100.0 * sx["kv_gbps"] / HBM_PEAK_GBPS, 2),
+                "merge_frac": sx["merge_frac"], "mfma_pct_bf16_peak": sx["mfma_pct_bf16_peak"],
+                "steps_per_s": round(1e3 / sx["ms_per_step"], 3),
+            }
+            cg.free()
+            del cg
+            torch.cuda.empty_cache()
+    out["per_config"] = per_config
+
     probe = hbm_read_probe(args.steps, args.warmup)
     out["hbm_read_probe"] = probe
     out["roofline"]["frac_of_probe"] = round(achieved / probe["gbps"], 4)
     if not args.no_cpu_baseline:
+        print("bench: cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+        out["cpu_baseline"]["single_thread_tiny"] = single_thread_tiny_oracle()
     print(json.dumps(out), flush=True)
 
 

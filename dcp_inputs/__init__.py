@@ -142,9 +142,10 @@ def _host_lib_handle() -> Optional[ctypes.CDLL]:
     global _host_lib
     if _host_lib is None and os.path.exists(HOST_LIB_PATH):
         lib = ctypes.CDLL(HOST_LIB_PATH)
-        lib.dcp_synth_host_rows.restype = ctypes.c_int
-        lib.dcp_synth_host_rows.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                            ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p]
+        for fn in (lib.dcp_synth_host_rows, lib.dcp_synth_host_rows_f64):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint64,
+                           ctypes.c_int32, ctypes.c_void_p]
         _host_lib = lib
     return _host_lib
 
@@ -168,6 +169,23 @@ def host_rows(row_ids, cols: int, seed: int, stream: int, mode: int = 0) -> np.n
                                      stream_key(seed, stream), mode, out.ctypes.data)
         if rc != 0:
             raise RuntimeError("dcp_synth_host_rows failed")
+    return out
+
+
+def host_rows_f64(row_ids, cols: int, seed: int, stream: int, mode: int = 0) -> np.ndarray:
+    """The values of host_rows (bf16) widened exactly to float64 [len(row_ids), cols]."""
+    if cols > MAX_COLS:
+        raise ValueError("at most %d columns per row" % MAX_COLS)
+    row_ids = np.ascontiguousarray(np.asarray(row_ids, dtype=np.uint64).reshape(-1))
+    lib = _host_lib_handle()
+    if lib is None:
+        return bf16_bits_to_f64(host_rows(row_ids, cols, seed, stream, mode))
+    out = np.empty((row_ids.size, cols), dtype=np.float64)
+    if row_ids.size:
+        rc = lib.dcp_synth_host_rows_f64(row_ids.ctypes.data, row_ids.size, cols,
+                                         stream_key(seed, stream), mode, out.ctypes.data)
+        if rc != 0:
+            raise RuntimeError("dcp_synth_host_rows_f64 failed")
     return out
 
 
@@ -195,6 +213,19 @@ def host_query(batch: int, heads: int, dim: int, seed: int) -> np.ndarray:
 def host_latent(b: int, tokens, dim: int, seed: int) -> np.ndarray:
     """bf16 bits [len(tokens), dim] of request ``b``'s latent rows at global positions ``tokens``."""
     return host_rows(latent_row_ids(b, tokens), dim, seed, STREAM_K)
+
+
+def host_latent_f64(b: int, tokens, dim: int, seed: int) -> np.ndarray:
+    """host_latent's values widened to float64."""
+    return host_rows_f64(latent_row_ids(b, tokens), dim, seed, STREAM_K)
+
+
+def host_gqa_kv_f64(b: int, tokens, num_kv_heads: int, dim: int, seed: int, stream: int) -> np.ndarray:
+    """host_gqa_kv's values widened to float64."""
+    t = np.asarray(tokens, dtype=np.uint64)
+    rows = ((_U64(b) << _U64(ROW_T_BITS)) + t)[:, None] * _U64(num_kv_heads) + \
+        np.arange(num_kv_heads, dtype=np.uint64)[None, :]
+    return host_rows_f64(rows.reshape(-1), dim, seed, stream).reshape(t.size, num_kv_heads, dim)
 
 
 def host_gqa_kv(b: int, tokens, num_kv_heads: int, dim: int, seed: int, stream: int) -> np.ndarray:

@@ -2,7 +2,8 @@
  * splitmix64 (Steele, Lea & Flood, OOPSLA 2014) at counter 3c+k, k = 0..2, with
  * c = row * 1024 + col; the twelve 16-bit fields form an Irwin-Hall(12) sum that is
  * centred and scaled to a unit-variance value, then rounded to bf16 (nearest-even).
- * mode 1 ("census") instead writes bit `col` of `row` (1.0 or 0.0) for col < 24, else 0. */
+ * mode 1 ("census") instead writes bit `col` of `row` (1.0 or 0.0) for col < 24, else 0.
+ * dcp_synth_host_rows_f64 writes the same bf16 values widened exactly to float64. */
 #include <stdint.h>
 
 #define GOLDEN 0x9E3779B97F4A7C15ULL
@@ -39,6 +40,23 @@ int dcp_synth_host_rows(const uint64_t* row_ids, int64_t n, int32_t cols, uint64
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) {
     for (int32_t c = 0; c < cols; ++c) out[i * cols + c] = gen_value(key, row_ids[i], (uint32_t)c, mode);
+  }
+  return 0;
+}
+
+static inline double bf16_to_f64(uint16_t b) {
+  union { uint32_t u; float f; } v;
+  v.u = (uint32_t)b << 16;
+  return (double)v.f;
+}
+
+int dcp_synth_host_rows_f64(const uint64_t* row_ids, int64_t n, int32_t cols, uint64_t key, int32_t mode,
+                            double* out) {
+  if (!row_ids || !out || n < 0 || cols <= 0 || cols > 1024) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    for (int32_t c = 0; c < cols; ++c)
+      out[i * cols + c] = bf16_to_f64(gen_value(key, row_ids[i], (uint32_t)c, mode));
   }
   return 0;
 }

@@ -121,14 +121,14 @@ def merge(O_parts, LSE_parts):
 def _query(wl, b: int, seed: int) -> np.ndarray:
     H = wl.num_q_heads
     rows = np.arange(b * H, (b + 1) * H, dtype=np.uint64)
-    return di.bf16_bits_to_f64(di.host_rows(rows, wl.qk_dim, seed, di.STREAM_Q))
+    return di.host_rows_f64(rows, wl.qk_dim, seed, di.STREAM_Q)
 
 
 def mla_inputs(wl, b: int, tokens, seed=None):
     """(q [H,576], K [T,1,576], V [T,1,v_dim]) in float64 for request ``b`` at global ``tokens``."""
     seed = wl.seed if seed is None else seed
     q = _query(wl, b, seed)
-    lat = di.bf16_bits_to_f64(di.host_latent(b, tokens, wl.qk_dim, seed))
+    lat = di.host_latent_f64(b, tokens, wl.qk_dim, seed)
     return q, lat[:, None, :], lat[:, None, :wl.v_dim]
 
 
@@ -136,10 +136,8 @@ def gqa_inputs(wl, b: int, tokens, seed=None):
     """(q [H,D], K [T,Hkv,D], V [T,Hkv,D]) in float64 for request ``b`` at global ``tokens``."""
     seed = wl.seed if seed is None else seed
     q = _query(wl, b, seed)
-    K = di.bf16_bits_to_f64(di.host_gqa_kv(b, tokens, wl.num_kv_heads, wl.qk_dim, seed,
-                                           di.STREAM_K))
-    V = di.bf16_bits_to_f64(di.host_gqa_kv(b, tokens, wl.num_kv_heads, wl.v_dim, seed,
-                                           di.STREAM_V))
+    K = di.host_gqa_kv_f64(b, tokens, wl.num_kv_heads, wl.qk_dim, seed, di.STREAM_K)
+    V = di.host_gqa_kv_f64(b, tokens, wl.num_kv_heads, wl.v_dim, seed, di.STREAM_V)
     return q, K, V
 
 

@@ -337,12 +337,9 @@ def _sample_requests(lengths, k=4):
     return sorted(idx)
 
 
-@pytest.mark.parametrize("name", ["mla_long_b128", "mla_c512", "mla_1m"])
-def test_full_size_mla(name):
-    """Full-size long-context MLA workloads in the launch configuration the benchmark
-    times (default partitions): rank 0 and rank N-1 partials and the N-way merge on
-    sampled requests (the longest, the shortest, the median, one more)."""
-    wl = di.WORKLOADS[name]
+def _full_size_partials(wl):
+    """Every rank's partials of a full-size workload in the launch configuration the
+    benchmark times (default partitions), ranks built one at a time, and their merge."""
     pg = _paged()
     q = pg.device_query(wl)
     sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
@@ -354,21 +351,100 @@ def test_full_size_mla(name):
         pg.run_partial(wl, rc, q, sl, o_all[r], l_all[r], ws)
         torch.cuda.synchronize()
         del rc
+        print("%s: rank %d done" % (wl.name, r), flush=True)
     om = torch.empty_like(o_all[0]); lm = torch.empty_like(l_all[0])
     dcp.dcp_merge(o_all, l_all, om, lm)
     torch.cuda.synchronize()
-    sample = _sample_requests(wl.lengths)
-    for b in sample:
-        for r in (0, wl.dcp_size - 1):
-            Or, Lr = oracle_rank(wl, b, r)
-            check_close(o_all[r, b].cpu().numpy(), l_all[r, b].cpu().numpy(), Or, Lr,
-                        "%s r%d b%d (L=%d)" % (name, r, b, wl.lengths[b]))
-        if wl.lengths[b] <= 300000:
-            Of, Lf = oracle.full_attention(wl, b)
-        else:  # merge of the oracle's own per-rank partials, for memory
-            pr = [oracle_rank(wl, b, r) for r in range(wl.dcp_size)]
-            Of, Lf = oracle.merge([p[0] for p in pr], [p[1] for p in pr])
-        check_close(om[b].cpu().numpy(), lm[b].cpu().numpy(), Of, Lf, "%s merged b%d" % (name, b))
+    assert dcp.dcp_workspace_errors(ws) == 0
+    return o_all.cpu().numpy(), l_all.cpu().numpy(), om.cpu().numpy(), lm.cpu().numpy()
+
+
+def test_full_size_long_b128_every_request():
+    """The 128-request long-context batch (64 heads, N=8, I=128): every request of every
+    rank against the oracle's rank partial, and every merged request against the oracle's
+    merge of its own rank partials (which equals full attention: blog Sec. 4.1, pinned on
+    the CPU)."""
+    wl = di.WORKLOADS["mla_long_b128"]
+    o_all, l_all, om, lm = _full_size_partials(wl)
+    for b in range(wl.batch):
+        parts = [oracle_rank(wl, b, r) for r in range(wl.dcp_size)]
+        for r in range(wl.dcp_size):
+            check_close(o_all[r, b], l_all[r, b], parts[r][0], parts[r][1], "long r%d b%d" % (r, b))
+        Of, Lf = oracle.merge([p[0] for p in parts], [p[1] for p in parts])
+        check_close(om[b], lm[b], Of, Lf, "long merged b%d (L=%d)" % (b, wl.lengths[b]))
+        if b % 16 == 15:
+            print("checked requests 0..%d" % b, flush=True)
+
+
+def test_full_size_c512_rank0_every_request():
+    """The 512-request batch: every request of rank 0 (and of rank N-1 on a sample) against
+    the oracle, and the merge on sampled requests (longest, shortest, median, more)."""
+    wl = di.WORKLOADS["mla_c512"]
+    o_all, l_all, om, lm = _full_size_partials(wl)
+    for b in range(wl.batch):
+        Or, Lr = oracle_rank(wl, b, 0)
+        check_close(o_all[0, b], l_all[0, b], Or, Lr, "c512 r0 b%d" % b)
+        if b % 64 == 63:
+            print("rank 0: checked requests 0..%d" % b, flush=True)
+    for b in _sample_requests(wl.lengths, 8):
+        parts = [oracle_rank(wl, b, r) for r in range(wl.dcp_size)]
+        r = wl.dcp_size - 1
+        check_close(o_all[r, b], l_all[r, b], parts[r][0], parts[r][1], "c512 r%d b%d" % (r, b))
+        Of, Lf = oracle.merge([p[0] for p in parts], [p[1] for p in parts])
+        check_close(om[b], lm[b], Of, Lf, "c512 merged b%d (L=%d)" % (b, wl.lengths[b]))
+
+
+def test_full_size_1m_every_rank_and_merge():
+    """The single 1,048,576-token request (128 heads, N=8, I=128): every rank's partial and
+    the merge against the oracle."""
+    wl = di.WORKLOADS["mla_1m"]
+    o_all, l_all, om, lm = _full_size_partials(wl)
+    parts = [oracle_rank(wl, 0, r) for r in range(wl.dcp_size)]
+    for r in range(wl.dcp_size):
+        check_close(o_all[r, 0], l_all[r, 0], parts[r][0], parts[r][1], "1m r%d" % r)
+    Of, Lf = oracle.merge([p[0] for p in parts], [p[1] for p in parts])
+    check_close(om[0], lm[0], Of, Lf, "1m merged")
+
+
+@pytest.mark.parametrize("name", ["mla_1m", "mla_long_b128"])
+def test_full_size_census_rank0(name):
+    """Census at the full shape in the benchmark's launch configuration: rank 0 of the
+    1M-token request (131,072 local tokens cut over every work partition and merged by the
+    split-K path) and of the 128-request batch; the exact token set of every request."""
+    _census_check(di.WORKLOADS[name], ranks=[0])
+
+
+def test_device_error_word_reports_clamped_inputs():
+    """Device-resident values the kernels clamp (an out-of-range page id, a local length
+    past the block-table row, a negative length) leave the call in bounds and set their
+    bit of the workspace's error word; a clean call sets none."""
+    pg = _paged()
+    for name in ("mla_tiny", "gqa_b32"):
+        wl = _wl(name, lengths=(1000, 3000, 500))
+        rc = pg.build_rank_cache(wl, 0)
+        q = pg.device_query(wl)
+        o = torch.empty((wl.batch, wl.num_q_heads, wl.v_dim), device="cuda")
+        lse = torch.empty((wl.batch, wl.num_q_heads), device="cuda")
+        ws = pg.workspace_for(wl)
+        sl = torch.tensor(np.asarray(wl.lengths, dtype=np.int32), device="cuda")
+        pg.run_partial(wl, rc, q, sl, o, lse, ws)
+        assert dcp.dcp_workspace_errors(ws) == 0
+        bt = rc.block_table.clone()
+        bt[1, 2] = -7
+        bt[2, 0] = rc.k_cache.shape[0] + 3
+        bad = pg.RankCache(0, rc.local_lens, bt, rc.k_cache, rc.v_cache, rc.poison_page)
+        pg.run_partial(wl, bad, q, sl, o, lse, ws)
+        assert dcp.dcp_workspace_errors(ws, clear=True) == dcp.DCP_DEVERR_PAGE_ID
+        assert dcp.dcp_workspace_errors(ws) == 0
+        sl_bad = torch.tensor([1000, -4, 500], dtype=torch.int32, device="cuda")
+        pg.run_partial(wl, rc, q, sl_bad, o, lse, ws)
+        torch.cuda.synchronize()
+        assert dcp.dcp_workspace_errors(ws, clear=True) == dcp.DCP_DEVERR_NEG_LENGTH
+        assert np.all(np.isneginf(lse[1].cpu().numpy())) and np.all(o[1].cpu().numpy() == 0)
+        short = rc.block_table[:, :2].contiguous()
+        cut = pg.RankCache(0, rc.local_lens, short, rc.k_cache, rc.v_cache, rc.poison_page)
+        pg.run_partial(wl, cut, q, sl, o, lse, ws)
+        assert dcp.dcp_workspace_errors(ws, clear=True) == dcp.DCP_DEVERR_TABLE_SHORT
 
 
 def _new_rows(wl, tokens):

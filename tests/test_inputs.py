@@ -29,6 +29,18 @@ def test_compiled_host_generator_matches_numpy():
     assert np.array_equal(di.host_rows(rows, 40, 0, 0, mode=1), di.census_rows_numpy(rows, 40))
 
 
+def test_float64_host_generator_is_the_widened_bf16_one():
+    rows = np.random.default_rng(3).integers(0, 2 ** 40, size=900).astype(np.uint64)
+    for cols, mode in ((576, 0), (128, 0), (40, 1)):
+        wide = di.host_rows_f64(rows, cols, 6, 2, mode=mode)
+        assert wide.dtype == np.float64
+        assert np.array_equal(wide, di.bf16_bits_to_f64(di.host_rows(rows, cols, 6, 2, mode=mode)))
+    t = np.array([0, 5, 77, 1 << 20])
+    assert np.array_equal(di.host_latent_f64(3, t, 576, 4), di.bf16_bits_to_f64(di.host_latent(3, t, 576, 4)))
+    assert np.array_equal(di.host_gqa_kv_f64(2, t, 4, 128, 4, di.STREAM_V),
+                          di.bf16_bits_to_f64(di.host_gqa_kv(2, t, 4, 128, 4, di.STREAM_V)))
+
+
 def test_generator_statistics_and_independence():
     z = di.bf16_bits_to_f64(di.host_rows(np.arange(4000, dtype=np.uint64), 576, 1, 1))
     assert abs(z.mean()) < 0.01 and abs(z.var() - 1.0) < 0.01 and np.abs(z).max() <= 6.0
