@@ -71,6 +71,8 @@ _SIGS = {
                                       _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "dcp_rescale_partial": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "dcp_sum_head_slice": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "dcp_decode_partial_noalloc": (_i32, [ctypes.POINTER(AttnDesc), _vp, _vp, _vp, _i64, _vp, _i32, _vp,
+                                          _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "dcp_workspace_init": (_i32, [_vp, _sz, _vp]),
     "dcp_workspace_errors": (_i32, [_vp, _sz, _vp, _i32, _vp]),
 }
@@ -206,6 +208,17 @@ def dcp_decode_partial(desc: AttnDesc, q, k_cache, v_cache, block_table, seq_len
         _dptr(block_table), block_table.shape[1], _dptr(seq_lens), batch, rank, num_ranks,
         interleave, num_partitions, _dptr(workspace), workspace.numel() * workspace.element_size(),
         _dptr(out_o), _dptr(out_lse), _stream(stream)))
+
+
+def dcp_decode_partial_noalloc(desc: AttnDesc, q, k_cache, v_cache, block_table, seq_lens, rank: int,
+                               num_ranks: int, interleave: int, out_o, out_lse, num_partitions: int = 0,
+                               stream=None) -> None:
+    """dcp_decode_partial with the library's static device scratch instead of a workspace."""
+    batch = q.shape[0]
+    _check("dcp_decode_partial_noalloc", lib().dcp_decode_partial_noalloc(
+        ctypes.byref(desc), _dptr(q), _dptr(k_cache), _dptr(v_cache), k_cache.shape[0],
+        _dptr(block_table), block_table.shape[1], _dptr(seq_lens), batch, rank, num_ranks,
+        interleave, num_partitions, _dptr(out_o), _dptr(out_lse), _stream(stream)))
 
 
 def dcp_append_kv(desc: AttnDesc, new_k, new_v, k_cache, v_cache, block_table, seq_lens,

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libdcp.so")
 SOURCES = ["dcp_api.hip", "mla_partial.hip", "gqa_partial.hip", "reduce.hip", "append.hip",
-           "merge_steps.hip"]
+           "merge_steps.hip", "noalloc.hip"]
 ARCH = os.environ.get("DCP_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are disabled: hipcc must not emit v_pk_{add,mul,fma}_f32.

@@ -207,6 +207,22 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
                                 void* workspace, size_t workspace_bytes, float* out_o,
                                 float* out_lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): dcp_decode_partial with the library's
+ * own static device scratch (72 MiB per device, held until the process ends) in place of
+ * the caller's workspace.  Arguments, outputs and errors as for dcp_decode_partial; a
+ * call whose workspace (dcp_decode_workspace_size) would exceed the scratch returns
+ * DCP_ERROR_WORKSPACE and runs nothing.  Allocates nothing: the first call on a device
+ * zeroes that device's scratch on `stream`.  Every call on a device shares its scratch,
+ * so calls that overlap on one GPU (different streams, or concurrent host threads
+ * without stream order between their work) race and give wrong results. */
+dcp_status_t dcp_decode_partial_noalloc(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
+                                        const void* v_cache, int64_t num_cache_blocks,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        const int32_t* seq_lens, int32_t batch, int32_t rank,
+                                        int32_t num_ranks, int32_t interleave, int32_t num_partitions,
+                                        float* out_o, float* out_lse, void* stream);
+
 /* Multi-token decode queries (speculative decoding / multi-token prediction; blog
  * Sec. 6): q_len >= 1 query tokens per request, the request's last q_len positions,
  * whose K/V rows are already in the cache (seq_lens counts them).  Query i (global
