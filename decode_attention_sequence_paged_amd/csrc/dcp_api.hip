@@ -96,18 +96,15 @@ int32_t default_parts(int32_t head_groups) {
   return p < 1 ? 1 : p;
 }
 
-// Workspace of a partial call: a 256-byte header (the device error word at offset 0),
-// the per-slot and per-request arrival counters of the in-kernel split-K merge, the
-// partition prefix, and the split pieces' LSEs and outputs.  dcp_workspace_init zeroes
-// it once; the kernels leave the counters at zero after every call.
+// Workspace of a partial call: a 256-byte header (the device error word at offset 0, which
+// dcp_workspace_init zeroes), the partition prefix, and the split pieces' LSEs and outputs.
 struct WsLayout {
-  size_t cnt, prefix, lse, o, total;
+  size_t prefix, lse, o, total;
 };
 
 WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
   WsLayout l;
-  l.cnt = 256;
-  l.prefix = l.cnt + align256(sizeof(uint32_t) * (2 * (size_t)parts + (size_t)batch));
+  l.prefix = 256;
   l.lse = l.prefix + align256(sizeof(int64_t) * (3 * (size_t)batch + 2));
   l.o = l.lse + align256(sizeof(float) * 2 * (size_t)parts * heads);
   l.total = l.o + align256(sizeof(float) * 2 * (size_t)parts * heads * v_dim);

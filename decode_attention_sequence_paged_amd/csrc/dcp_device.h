@@ -151,7 +151,7 @@ struct SpanLoc {
 // *err_word the bits of the lengths it had to clamp.  s_scan must hold blockDim.x / 64
 // int64 values; s_loc four int64 values.
 template <int NT>
-__device__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
+__device__ __forceinline__ SpanLoc locate_span(const PartitionArgs& a, int64_t w, int64_t* prefix_out,
                                uint32_t* err_word, int64_t* s_scan, int64_t* s_loc) {
   constexpr int64_t kCountMask = (int64_t(1) << kCountBits) - 1;
   const int tid = threadIdx.x;
@@ -356,12 +356,15 @@ __device__ __forceinline__ uint32_t lds_addr(const DCP_LDS void* p) { return (ui
 // reads, streaming them past the caches raised the attained HBM bandwidth by 7-11%
 // (measured); pages that the head groups of a span share through their XCD's L2 are
 // read with the default policy, which keeps them there for the partner.
+// `base` must be wave-uniform; it is passed through readfirstlane so that it stays in scalar
+// registers whatever the compiler concludes about the control flow around the call.
 template <bool kStream>
 __device__ __forceinline__ void copy16(const uint8_t* base, uint32_t off, uint32_t lds_dst) {
+  const uint8_t* sbase = (const uint8_t*)uniform64((int64_t)base);
   if constexpr (kStream)
-    asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(base), "{m0}"(lds_dst));
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" : : "v"(off), "s"(sbase), "{m0}"(lds_dst));
   else
-    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds_dst));
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(sbase), "{m0}"(lds_dst));
 }
 __device__ __forceinline__ void zero_lds16(uint32_t addr) {
   asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(u32x4{0u, 0u, 0u, 0u}) : "memory");

@@ -16,7 +16,7 @@ namespace {
 // 72 MiB: the workspace of every supported single-token shape at the default work
 // partitions, for up to 65,536 requests.  The split pieces take at most 64 MiB (2 slots x
 // 256 partitions x 64 heads x 512 dims x 4 bytes; 128 or more heads use proportionally
-// fewer partitions per head group), the partition prefix 1.5 MiB, the counters 257 KiB.
+// fewer partitions per head group), the partition prefix 1.5 MiB.
 constexpr size_t kScratchBytes = size_t(72) << 20;
 constexpr int kMaxDevices = 64;
 
@@ -28,8 +28,7 @@ std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once known
 
 // Device address of this device's scratch.  The first call on a device looks it up and
-// zeroes the array on `stream` (the kernels' counters and error word must start at zero
-// and are left at zero by every call).
+// zeroes the array on `stream` (the device error word in its header starts clear).
 dcp_status_t current_scratch(hipStream_t stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DCP_ERROR_HIP;

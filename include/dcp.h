@@ -146,8 +146,7 @@ typedef enum {
 } dcp_device_error_t;
 
 /* Zero a workspace for dcp_decode_partial / dcp_decode_partial_mtp (device; enqueued
- * on `stream`, no allocation).  Needed once after allocation; the calls keep the
- * workspace's counters at zero themselves.
+ * on `stream`, no allocation), so that its device error word starts clear.
  * Errors: INVALID_VALUE for a NULL or misaligned workspace or zero bytes; HIP. */
 dcp_status_t dcp_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
@@ -185,11 +184,11 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *                request cut between partitions is reduced in a second kernel
  *                (split-K).
  *   workspace    device, >= dcp_decode_workspace_size(desc, batch, num_partitions)
- *                bytes, 256-byte aligned, zeroed once by dcp_workspace_init before its
- *                first use (it holds counters the kernels leave at zero after every
- *                call, and the device error word).  Calls that share a workspace
- *                must be ordered (one stream); a workspace is not shared between
- *                calls that may run concurrently.
+ *                bytes, 256-byte aligned.  Its first 256 bytes hold the device error
+ *                word, meaningful once dcp_workspace_init has zeroed it; nothing else
+ *                in it needs initialisation.  Calls that share a workspace must be
+ *                ordered (one stream); a workspace is not shared between calls that
+ *                may run concurrently.
  *   out_o        device fp32 [batch, H, v_dim], written: normalised partial output
  *                O_r = sum_t p_t v_t / sum_t p_t over the rank's tokens.
  *   out_lse      device fp32 [batch, H], written: LSE_r = ln sum_t exp(s_t),
