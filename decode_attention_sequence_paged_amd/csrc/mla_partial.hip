@@ -816,6 +816,15 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
 #pragma unroll
           for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[m][hb] = mfma16x16x32(a, pP[hb], oacc[m][hb]);
         }
+        // keep the V^T reads kPfV blocks ahead of the MFMAs (the scheduler would otherwise
+        // sink them next to their use and expose the LDS latency block by block)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPfV, 0);
+#pragma unroll
+        for (int m = 0; m < kDimBlocks - kPfV; ++m) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, kHeadBlocks, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kHeadBlocks * (kDimBlocks < kPfV ? kDimBlocks : kPfV), 0);
         if (cur.t == cur.ntile - 1 || i == total - 1) {
           // 1/l of every head leaves LDS now: the next tile of this parity overwrites it
           pend_inv = *(const DCP_LDS f32x4*)&s_inv[par][l16][0];
