@@ -9,7 +9,7 @@ before timing starts.
 Printed as one JSON line:
   value            KV bytes of all ranks / step time (GB/s): whole-job throughput
   ms_per_step      wall time of one step (K steps bracketed by synchronize)
-  rank0_kv_gbps    local-shard KV GB/s of rank 0's partial call (HIP events)
+  rank0_kv_gbps    local-shard KV GB/s of rank 0's partial call (HIP events, median)
   roofline         the partial-attention call against the 8 TB/s HBM peak
   cpu_baseline     the float64 oracle on the host cores, per-rank partials of the batch
   hbm_read_probe   attainable HBM read bandwidth of plain streaming loads on this device
@@ -20,11 +20,13 @@ each request-length band of the pages' comparison by sequence length (<32k, 32-6
 the synthetic mix restricted to the band, as many as give rank 0 about 1.25M tokens.
 
 With --next it instead prints one JSON line timing the steps next to the hot path on the
-long-context MLA batch: rank 0's partial for 2 and 4 query tokens per request (multi-token
-decode queries, causal by global position; also on the GQA batch), the append of every request's newest latent
-row into its owner rank's page (all N ranks' calls), and the merge as per-rank steps
-(global LSE from the gathered LSEs, local rescale with fp32 or bf16 transport, one rank's
-head slice of the sum) beside the fused N-way merge.
+long-context MLA batch: the partial calls of ranks 0..3 for 1, 2 and 4 query tokens per
+request (multi-token decode queries, causal by global position; also on the GQA batch,
+all four ranks), the append of every request's newest latent row into its owner rank's
+page (all N ranks' calls), and the merge as per-rank steps (global LSE from the gathered
+LSEs, local rescale with fp32 or bf16 transport, one rank's head slice of the sum) beside
+the fused N-way merge.  Call times there are medians over the calls, events around every
+call, no synchronisation between the calls.
 """
 from __future__ import annotations
 
@@ -188,7 +190,7 @@ def run_bands(args):
             paged.run_partial(wl, rc, q, sl, o, lse, ws)
             b.record()
         torch.cuda.synchronize()
-        t = float(np.mean([a.elapsed_time(b) for a, b in evs]))  # ms
+        t = float(np.median([a.elapsed_time(b) for a, b in evs]))  # ms
         H = wl.num_q_heads
         pages = int(((rc.local_lens + wl.block_size - 1) // wl.block_size).sum())
         kv = rc.total_local * wl.qk_dim * 2
@@ -217,7 +219,8 @@ def run_bands(args):
 
 
 def _event_ms(fn, steps: int, warmup: int) -> float:
-    """Mean milliseconds of fn() over `steps` calls, HIP events on the launch stream."""
+    """Median milliseconds of fn() over `steps` calls, HIP events on the launch stream around
+    every call, no synchronisation between the calls."""
     import torch
     for _ in range(warmup):
         fn()
@@ -229,7 +232,26 @@ def _event_ms(fn, steps: int, warmup: int) -> float:
         fn()
         b.record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def _event_ms_calls(fns, steps: int, warmup: int) -> np.ndarray:
+    """Milliseconds of each call of fns (called in turn, `steps` rounds), HIP events on the
+    launch stream around every call, no synchronisation between the calls; [steps, len(fns)]."""
+    import torch
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+           for _ in range(steps)]
+    for row in evs:
+        for (a, b), fn in zip(row, fns):
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    return np.array([[a.elapsed_time(b) for a, b in row] for row in evs])
 
 
 def hbm_read_probe(steps: int, warmup: int, nbytes: int = 4 << 30):
@@ -272,10 +294,13 @@ def run_next(args):
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": describe(wl)}}
 
-    # multi-token decode queries: rank 0's call for q_len = 1, 2, 4
-    rc = paged.build_rank_cache(wl, 0)
-    pages = int(((rc.local_lens + bs - 1) // bs).sum())
-    kv = rc.total_local * Dqk * 2
+    # multi-token decode queries, q_len = 1, 2, 4: the calls of ranks 0..3 in turn, events
+    # around every call; median over the calls of all four ranks
+    NR = min(N, 4)
+    rcs = [paged.build_rank_cache(wl, r) for r in range(NR)]
+    pages = np.mean([int(((rc.local_lens + bs - 1) // bs).sum()) for rc in rcs])
+    local = float(np.mean([rc.total_local for rc in rcs]))
+    kv = local * Dqk * 2
     mtp = []
     for q_len in (1, 2, 4):
         qw = di.Workload(**dict(wl.__dict__, batch=B * q_len, lengths=tuple(wl.lengths) * q_len))
@@ -283,26 +308,30 @@ def run_next(args):
         ws = paged.workspace_for(wl, 0, q_len=q_len)
         o = torch.empty((B, q_len, H, Dv), device="cuda")
         lse = torch.empty((B, q_len, H), device="cuda")
-        t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl,
-                                                          0, N, wl.interleave, ws, o, lse),
-                      args.steps, args.warmup)
+        fns = [(lambda rc=rc: dcp.dcp_decode_partial_mtp(desc, q, rc.k_cache, None, rc.block_table, sl,
+                                                         rc.rank, N, wl.interleave, ws, o, lse))
+               for rc in rcs]
+        ms = _event_ms_calls(fns, args.steps, args.warmup)
+        t = float(np.median(ms))
         call = kv + B * q_len * H * (Dqk * 2 + Dv * 4 + 4) + pages * 4
-        mtp.append({"q_len": q_len, "score_rows_per_request": q_len * H, "rank0_call_ms": round(t, 4),
-                    "rank0_kv_gbps": round(kv / (t * 1e-3) / 1e9, 1),
+        mtp.append({"q_len": q_len, "score_rows_per_request": q_len * H,
+                    "call_ms_median": round(t, 4), "call_ms_p10": round(float(np.percentile(ms, 10)), 4),
+                    "call_ms_p90": round(float(np.percentile(ms, 90)), 4),
+                    "kv_gbps": round(kv / (t * 1e-3) / 1e9, 1),
                     "roofline_frac": round(call / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                    "flops_per_s": round(2.0 * q_len * H * (Dqk + Dv) * rc.total_local / (t * 1e-3), 1)})
-        del q, ws, o, lse
-    out["multi_token_queries"] = mtp
-    del rc
+                    "flops_per_s": round(2.0 * q_len * H * (Dqk + Dv) * local / (t * 1e-3), 1)})
+        del q, ws, o, lse, fns
+    out["multi_token_queries"] = {"ranks": NR, "rows": mtp}
+    del rcs
     torch.cuda.empty_cache()
 
     # GQA multi-token queries (one single-token pass per query token): rank 0 of the GQA batch
     gw = di.WORKLOADS["gqa_b32"]
     gdesc = paged.desc_for(gw)
     gsl = torch.tensor(np.asarray(gw.lengths, dtype=np.int32), device="cuda")
-    grc = paged.build_rank_cache(gw, 0)
+    grcs = [paged.build_rank_cache(gw, r) for r in range(gw.dcp_size)]
     GB, GH = gw.batch, gw.num_q_heads
-    gkv = grc.total_local * gw.num_kv_heads * (gw.qk_dim + gw.v_dim) * 2
+    gkv = float(np.mean([grc.total_local for grc in grcs])) * gw.num_kv_heads * (gw.qk_dim + gw.v_dim) * 2
     gmtp = []
     for q_len in (1, 2, 4):
         qw = di.Workload(**dict(gw.__dict__, batch=GB * q_len, lengths=tuple(gw.lengths) * q_len))
@@ -310,16 +339,17 @@ def run_next(args):
         ws = paged.workspace_for(gw, 0, q_len=q_len)
         o = torch.empty((GB, q_len, GH, gw.v_dim), device="cuda")
         lse = torch.empty((GB, q_len, GH), device="cuda")
-        t = _event_ms(lambda: dcp.dcp_decode_partial_mtp(gdesc, q, grc.k_cache, grc.v_cache,
-                                                          grc.block_table, gsl, 0, gw.dcp_size,
-                                                          gw.interleave, ws, o, lse),
-                      args.steps, args.warmup)
-        gmtp.append({"q_len": q_len, "passes": q_len, "rank0_call_ms": round(t, 4),
-                     "rank0_kv_gbps_per_query_token": round(gkv * q_len / (t * 1e-3) / 1e9, 1),
+        fns = [(lambda grc=grc: dcp.dcp_decode_partial_mtp(gdesc, q, grc.k_cache, grc.v_cache,
+                                                           grc.block_table, gsl, grc.rank, gw.dcp_size,
+                                                           gw.interleave, ws, o, lse))
+               for grc in grcs]
+        t = float(np.median(_event_ms_calls(fns, args.steps, args.warmup)))
+        gmtp.append({"q_len": q_len, "passes": q_len, "call_ms_median": round(t, 4),
+                     "kv_gbps_per_query_token": round(gkv * q_len / (t * 1e-3) / 1e9, 1),
                      "ms_per_query_token": round(t / q_len, 4)})
-        del q, ws, o, lse
-    out["gqa_multi_token_queries"] = {"workload": describe(gw), "rows": gmtp}
-    del grc
+        del q, ws, o, lse, fns
+    out["gqa_multi_token_queries"] = {"workload": describe(gw), "ranks": gw.dcp_size, "rows": gmtp}
+    del grcs
     torch.cuda.empty_cache()
 
     # KV append: every rank's call; only the owner of position L-1 writes a request's row
