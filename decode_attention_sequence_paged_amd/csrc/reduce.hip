@@ -1,9 +1,9 @@
 // Log-sum-exp merges and shard-map kernels.
 //
 // The merge rule is the one the vLLM blog "Efficient Decode Context Parallelism
-// with vLLM for Long Context Workloads" states in Sec. 4.1 ("AllGather +
-// ReduceScatter"): partial outputs over disjoint token sets are reweighted by
-// their LSE values (the online-softmax trick) and summed,
+// with vLLM for Long Context Workloads" states in Sec. 4.1 (its all-gather and
+// reduce-scatter step): partial outputs over disjoint token sets are reweighted by
+// their LSE values (the rescaling online softmax also uses) and summed,
 //   LSE = ln sum_i exp(LSE_i),   O = sum_i exp(LSE_i - LSE) O_i.
 // It serves twice: inside a rank, to join the pieces of a request that several
 // work partitions computed (split-K), and across the N ranks.

@@ -11,8 +11,8 @@
  *   - Sec. 4.1 ("Decode Context Parallelism Process"), "Compute": each GPU attends
  *     the full single-token query against its local KV slice and produces a
  *     partial output plus a log-sum-exp (LSE) per head; then the LSE values
- *     reweight and merge the partials (the online-softmax trick) into the true
- *     output.
+ *     reweight and merge the partials (the rescaling online softmax also uses) into
+ *     the exact full-context result.
  *   - Sec. 5.3 (MLA backend): one latent KV vector shared by every query head;
  *     Sec. 5.4 (GQA backend): each KV head is shared by a group of query heads.
  *   - The vLLM-Ascend "Decode Context Parallel Guide", Constraints: the KV cache

@@ -13,8 +13,8 @@ Context Workloads"):
   positions of every request; Sec. 2.2: each GPU stores only 1/N of a request's KV.
 * Sec. 4.1 ("Decode Context Parallelism Process"): every GPU attends the full
   single-token query against its local KV slice, producing a partial output and a
-  log-sum-exp; the LSE values reweight and merge the partials (the online-softmax
-  trick) into the true output.
+  log-sum-exp; the LSE values reweight and merge the partials (the rescaling online
+  softmax also uses) into the exact full-context result.
 * Sec. 5.3 (MLA backend): one latent KV vector shared by all query heads.
 * Sec. 5.4 (GQA backend): each KV head is shared by (broadcast to) its group of
   query heads.

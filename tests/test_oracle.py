@@ -8,8 +8,8 @@ planted mistake fails at least one pin.
 Independent references used here:
 * the pages' worked ownership example (tests/golden/contiguous_split_200k_4gpu.txt);
 * the pages' statement that each GPU holds 1/N of a request's KV (blog Sec. 2.2);
-* the pages' statement that the reweighted merge of the partials is the true output
-  (blog Sec. 4.1): sharded-then-merged must equal unsharded attention;
+* the pages' statement that the reweighted merge of the partials is the exact
+  full-context result (blog Sec. 4.1): sharded-then-merged must equal unsharded attention;
 * torch's CPU ``scaled_dot_product_attention`` and scipy's ``logsumexp`` in float64;
 * closed forms (q = 0, constant V, one token, two tokens, dominant logit) and bounds;
 * brute force in pure-Python loops on tiny inputs.
