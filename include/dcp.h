@@ -214,7 +214,9 @@ dcp_status_t dcp_decode_partial(const dcp_attn_desc_t* desc, const void* q, cons
  * DCP_ERROR_WORKSPACE and runs nothing.  Allocates nothing: the first call on a device
  * zeroes that device's scratch on `stream`.  Every call on a device shares its scratch,
  * so calls that overlap on one GPU (different streams, or concurrent host threads
- * without stream order between their work) race and give wrong results. */
+ * without stream order between their work) race and give wrong results.  The device
+ * error word of the scratch (see dcp_workspace_errors) is not exposed: callers that
+ * want the device-side checks pass their own workspace to dcp_decode_partial. */
 dcp_status_t dcp_decode_partial_noalloc(const dcp_attn_desc_t* desc, const void* q, const void* k_cache,
                                         const void* v_cache, int64_t num_cache_blocks,
                                         const int32_t* block_table, int32_t max_blocks_per_seq,
