@@ -20,6 +20,7 @@ constexpr int32_t kMaxParts = 1 << 16;
 constexpr int32_t kMaxMlaRows = 512;  // MLA score rows (query tokens x heads) per request
 constexpr int64_t kMaxMtpRows = kMaxMlaRows;
 constexpr int32_t kMaxGqaQueryTokens = 64;  // query tokens per request of a GQA multi-token call
+constexpr int32_t kGqaMaxQueryBlock = 2;    // query tokens per GQA pass (MFMA column blocks)
 constexpr int32_t kMaxDevices = 64;
 
 // Cache of the compute-unit count per device (filled on first use; concurrent callers
@@ -112,9 +113,10 @@ WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
 }
 
 // Multi-token decode queries.  MLA: q_len query tokens of num_q_heads heads become
-// q_len * num_q_heads score rows of one pass.  GQA: one pass per query token (the
-// kernel keeps a KV head's query heads on the 16 MFMA columns), so the shapes are
-// those of a single-token call.
+// q_len * num_q_heads score rows of one pass.  GQA: passes of up to two query tokens
+// (the kernel keeps a KV head's query heads on the 16 MFMA columns, one column block
+// per query token), so the head shapes are those of a single-token call and the
+// workspace holds the pieces of one pass.
 dcp_status_t check_q_len(const dcp_attn_desc_t* d, int32_t q_len, dcp_attn_desc_t* rows) {
   *rows = *d;
   if (q_len < 1) return DCP_ERROR_INVALID_VALUE;
@@ -124,6 +126,12 @@ dcp_status_t check_q_len(const dcp_attn_desc_t* d, int32_t q_len, dcp_attn_desc_
   if (d->num_q_heads < 1 || (int64_t)q_len * d->num_q_heads > kMaxMtpRows) return DCP_ERROR_NOT_SUPPORTED;
   rows->num_q_heads = q_len * d->num_q_heads;
   return DCP_SUCCESS;
+}
+
+// Piece rows per request in the workspace: the score rows of the pass with the most.
+int32_t workspace_rows(const dcp_attn_desc_t* rows, int32_t q_len) {
+  if (rows->kind != DCP_KV_GQA) return rows->num_q_heads;
+  return (q_len < kGqaMaxQueryBlock ? q_len : kGqaMaxQueryBlock) * rows->num_q_heads;
 }
 
 dcp_status_t check_shard_args(int32_t num_ranks, int32_t interleave, int32_t rank) {
@@ -251,7 +259,7 @@ size_t dcp_decode_workspace_size_mtp(const dcp_attn_desc_t* desc, int32_t q_len,
   if (check_desc(&d, &groups) != DCP_SUCCESS) return 0;
   if (batch < 0 || batch > kMaxBatch || num_partitions < 0 || num_partitions > kMaxParts) return 0;
   const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
-  return ws_layout(batch, parts, d.num_q_heads, d.v_dim).total;
+  return ws_layout(batch, parts, workspace_rows(&d, q_len), d.v_dim).total;
 }
 
 size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch, int32_t num_partitions) {
@@ -285,7 +293,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15) return DCP_ERROR_INVALID_VALUE;
   if (((uintptr_t)out_o & 15) || ((uintptr_t)out_lse & 3)) return DCP_ERROR_INVALID_VALUE;
   const int32_t parts = num_partitions ? num_partitions : default_parts(groups);
-  const WsLayout wl = ws_layout(batch, parts, d.num_q_heads, d.v_dim);
+  const WsLayout wl = ws_layout(batch, parts, workspace_rows(&d, q_len), d.v_dim);
   if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < wl.total) return DCP_ERROR_WORKSPACE;
 
   uint8_t* ws = (uint8_t*)workspace;
@@ -303,6 +311,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   p.num_head_groups = groups;
   p.q_len = q_len;
   p.heads_per_token = desc->num_q_heads;
+  p.q_block = 1;
   p.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   p.part.seq_lens = seq_lens;
   p.part.batch = batch;
@@ -346,22 +355,32 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
     return hip_status(dcp::launch_split_reduce(r, s));
   }
   // GQA: query token i of a request at global length L sees the positions <= L - q_len
-  // + i, i.e. the single-token problem at length L - (q_len - 1 - i).  One pass per
-  // query token, each over its own slices of q [B, q_len, H, D] and of the outputs
+  // + i.  Passes of qb = 2 or 1 consecutive query tokens i0 .. i0 + qb - 1: the
+  // partition covers the pass's newest token's positions (length L - (q_len - i0 - qb))
+  // and the kernel masks, for each older token, the newest positions it may not see.
+  // Each pass has its own slices of q [B, q_len, H, D] and of the outputs
   // [B, q_len, H, .]; the passes reuse the workspace in stream order.
   p.q_len = 1;
-  for (int32_t i = 0; i < q_len; ++i) {
-    p.part.len_offset = q_len - 1 - i;
-    p.q = (const uint16_t*)q + (int64_t)i * d.num_q_heads * d.qk_dim;
-    p.q_req_stride = (int64_t)q_len * d.num_q_heads * d.qk_dim;
-    p.out_o = out_o + (int64_t)i * d.num_q_heads * d.v_dim;
-    p.out_lse = out_lse + (int64_t)i * d.num_q_heads;
-    p.out_req_rows = (int64_t)q_len * d.num_q_heads;
+  p.q_req_stride = (int64_t)q_len * d.num_q_heads * d.qk_dim;
+  p.out_req_rows = (int64_t)q_len * d.num_q_heads;
+  r.out_req_rows = p.out_req_rows;
+  for (int32_t i0 = 0; i0 < q_len;) {
+    const int32_t left = q_len - i0;
+    const int32_t qb = left >= kGqaMaxQueryBlock ? kGqaMaxQueryBlock : 1;
+    p.q_block = qb;
+    p.part.len_offset = q_len - i0 - qb;
+    // a request's query slices and output rows grow with the pass's query tokens
+    p.part.req_weight = request_weight(&d) * qb;
+    r.req_weight = p.part.req_weight;
+    p.q = (const uint16_t*)q + (int64_t)i0 * d.num_q_heads * d.qk_dim;
+    p.out_o = out_o + (int64_t)i0 * d.num_q_heads * d.v_dim;
+    p.out_lse = out_lse + (int64_t)i0 * d.num_q_heads;
+    r.num_heads = qb * d.num_q_heads;
     r.out_o = p.out_o;
     r.out_lse = p.out_lse;
-    r.out_req_rows = p.out_req_rows;
     if (dcp::launch_gqa_partial(p, s) != hipSuccess) return DCP_ERROR_HIP;
     if (dcp::launch_split_reduce(r, s) != hipSuccess) return DCP_ERROR_HIP;
+    i0 += qb;
   }
   return DCP_SUCCESS;
 }

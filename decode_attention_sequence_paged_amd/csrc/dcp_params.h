@@ -29,13 +29,15 @@ struct PartialParams {
   int32_t num_head_groups;  // work-groups sharing one span (disjoint head sets)
   int32_t q_len;            // query tokens per request (1: single-token decode)
   int32_t heads_per_token;  // query heads per query token; rows = q_len * heads_per_token
+  int32_t q_block;          // GQA: query tokens of this pass (1 or 2), on consecutive MFMA
+                            // column blocks; its pieces have q_block * num_q_heads rows
   float scale_log2;         // softmax_scale * log2(e)
   PartitionArgs part;
   float* out_o;             // [B, H, v_dim]
   float* out_lse;           // [B, H]
-  int64_t q_req_stride;     // GQA: query elements between consecutive requests (H * qk_dim unless a
-                            // query token of a multi-token batch)
-  int64_t out_req_rows;     // GQA: output rows between consecutive requests (H unless likewise)
+  int64_t q_req_stride;     // GQA: query elements between consecutive requests (q_len * H * qk_dim;
+                            // the pass's q_block tokens are consecutive, H * qk_dim apart)
+  int64_t out_req_rows;     // GQA: output rows between consecutive requests (q_len * H)
   uint32_t* ws_err;         // device error word (dcp_device_error_t bits)
   int64_t* ws_prefix;       // [3 B + 2]: tile prefix, weighted prefix, span range of each request
   float* ws_lse;            // [2P, H]
@@ -51,7 +53,7 @@ struct SplitReduceParams {
   int32_t batch, num_heads, v_dim, num_parts, req_weight;
   int32_t xcd_weighted;      // as PartitionArgs::xcd_weighted of the partial call
   int64_t out_req_rows;      // output rows between consecutive requests (num_heads, or q_len *
-                             // num_heads for one query token of a multi-token GQA batch)
+                             // query heads for a pass of a multi-token GQA call)
   float* out_o;              // [B, H, v_dim]
   float* out_lse;            // [B, H]
 };

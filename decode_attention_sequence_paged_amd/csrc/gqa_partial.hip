@@ -30,6 +30,14 @@
 //  * Rows of a request's partial last tile past its end are copied from the page
 //    (always inside the pool) and made inert: scores -inf, V part zeroed in LDS.
 //    Finished pieces are stored after the next barrier, ahead of the next copies.
+//  * Multi-token decode queries (blog Sec. 6): QB query tokens of a request (QB = 1 or
+//    2) go on QB consecutive MFMA column blocks of the same KV head, so a pass streams
+//    the pages once for both: every K and V^T operand read feeds QB MFMAs.  (Four
+//    tokens per pass need more than 256 VGPRs; the compiler then parks values in
+//    accumulation registers, and with the query slices loaded by inline asm it could
+//    move a slice register before its load has landed, so passes stop at two.)  Query token i sees the global positions <= L - q_len + i; the pass's
+//    partition covers its newest token's positions and the older tokens' columns
+//    mask the few newest positions they may not see.
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -66,8 +74,9 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
-template <int KVW>
+template <int KVW, int QB>
 __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams p) {
+  static_assert(QB == 1 || QB == 2, "query tokens per pass");
   using C = Cfg<KVW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   __shared__ int64_t s_scan[C::kThreads];
@@ -98,6 +107,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   const bool head_ok = l16 < G;
   const int head = g * G + (head_ok ? l16 : 0);  // this lane's query head (S^T column)
   const int64_t row_stride = (int64_t)Hkv * kHeadBytes;  // bytes between token rows in the pool
+  const int rows = QB * H;  // piece rows of a request: query token c's head h is row c H + h
   const int64_t page_bytes = (int64_t)bs * row_stride;
   DCP_LDS uint8_t* lds = (DCP_LDS uint8_t*)smem;
 
@@ -170,41 +180,63 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   // compiler's wait counting (which cannot see the copies either) does not drain
   // the ring before every use; the next request's slice goes to qnext ahead of a
   // copy round, and the loop's own wait covers it before it moves into qreg.
-  bf16x8 qreg[4], qnext[4];
-  auto load_q = [&](bf16x8 (&dst)[4], int b) {
-    const uint16_t* qp = p.q + (int64_t)b * p.q_req_stride + (int64_t)head * kD + 8 * q4;
+  // Column block c holds query token c of the pass (its slice QB * ... apart: the
+  // tokens of a request are consecutive in q).
+  bf16x8 qreg[QB][4], qnext[QB][4];
+  auto load_q = [&](bf16x8 (&dst)[QB][4], int b) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[s]) : "v"(qp), "n"(64 * s) : "memory");
+    for (int c = 0; c < QB; ++c) {
+      const uint16_t* qp = p.q + (int64_t)b * p.q_req_stride + ((int64_t)c * H + head) * kD + 8 * q4;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[c][s]) : "v"(qp), "n"(64 * s) : "memory");
+    }
   };
-  auto settle = [&](bf16x8 (&r)[4]) {
+  auto settle = [&](bf16x8 (&r)[QB][4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(r[s]));
+    for (int c = 0; c < QB; ++c)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(r[c][s]));
   };
 
-  f32x4 oacc[8];
+  f32x4 oacc[QB][8];
+  float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) oacc[m] = f32x4{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int c = 0; c < QB; ++c) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) oacc[c][m] = f32x4{};
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+  }
 
   // Finished pieces are stored after the next barrier, before that iteration's copies.
+  // Query token c's row is H rows after token c - 1's, in the outputs and the pieces.
   bool pend = false;
-  float pend_inv = 0.f, pend_lse = 0.f;
-  float* pend_o = nullptr;
+  float pend_inv[QB], pend_lse[QB];
+  float* pend_o = nullptr;  // token 0's row
   float* pend_l = nullptr;
   auto flush_piece = [&]() {
     if (pend) {
       if (head_ok) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m) *(f32x4*)(pend_o + 16 * m) = oacc[m] * pend_inv;
-        if (q4 == 0) *pend_l = pend_lse;
+        for (int c = 0; c < QB; ++c) {
+#pragma unroll
+          for (int m = 0; m < 8; ++m)
+            *(f32x4*)(pend_o + (int64_t)c * H * kD + 16 * m) = oacc[c][m] * pend_inv[c];
+          if (q4 == 0) pend_l[c * H] = pend_lse[c];
+        }
       }
 #pragma unroll
-      for (int m = 0; m < 8; ++m) oacc[m] = f32x4{};
+      for (int c = 0; c < QB; ++c)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) oacc[c][m] = f32x4{};
       pend = false;
     }
   };
+  // Local tokens from which some column of the request may have to be masked: those
+  // standing for the pass's QB - 1 newest positions (set per request).
+  int mask_b = -1;
+  int64_t mask_from = 0;
 
   // Zero the V rows nvalid..15 of the tile at `vb` (the V half of a stage).
   auto zero_tail = [&](DCP_LDS uint8_t* vb, int nvalid) {
@@ -236,7 +268,9 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
     if (q_moved && i > 0) {
       settle(qnext);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) qreg[s] = qnext[s];
+      for (int c = 0; c < QB; ++c)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qreg[c][s] = qnext[c][s];
     }
     settle(qreg);
     q_moved = false;
@@ -262,39 +296,81 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       wg_barrier();
     }
 
-    // ---- S^T [16 tokens x 16 heads]
-    f32x4 sacc = f32x4{};
+    // ---- S^T [16 tokens x 16 heads] of each query token; a K operand serves all QB
+    f32x4 sacc[QB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sacc = mfma16x16x32(*(const DCP_LDS bf16x8*)(kb + ka[s]), qreg[s], sacc);
-
-    // ---- online softmax (base 2); lane: head l16, tokens 4 q4 + j
-    float x[4];
+    for (int c = 0; c < QB; ++c) sacc[c] = f32x4{};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = 4 * q4 + j < nvalid ? sacc[j] * p.scale_log2 : -INFINITY;
-    float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    mloc = max_over_groups(mloc);
-    const float m_new = mloc > m_run + kRescaleSlack ? mloc : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    float lsum = 0.f;
-    bf16x4 pb;
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 ka_s = *(const DCP_LDS bf16x8*)(kb + ka[s]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pr = fast_exp2(x[j] - m_new);
-      lsum += pr;
-      pb[j] = (__bf16)pr;
+      for (int c = 0; c < QB; ++c) sacc[c] = mfma16x16x32(ka_s, qreg[c][s], sacc[c]);
     }
-    lsum = sum_over_groups(lsum);
-    l_run = l_run * alpha + lsum;
-    if (__any(m_new != m_run)) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) oacc[m] *= alpha;
-    }
-    m_run = m_new;
 
-    // ---- O^T [128 dims x 16 heads] += V^T [128 x 16 tokens] P^T [16 x 16]
+    // ---- masks: rows past the request's end; with QB > 1, query token c sees the
+    // global positions <= Lg - QB + c (Lg: the pass's length, its newest token's)
+    float x[QB][4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      oacc[m] = mfma16x16x16(__builtin_bit_cast(bf16x4, lds_read_tr16(vb + va[m])), pb, oacc[m]);
+    for (int c = 0; c < QB; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[c][j] = 4 * q4 + j < nvalid ? sacc[c][j] * p.scale_log2 : -INFINITY;
+    if constexpr (QB > 1) {
+      const int N = p.part.num_ranks, I = p.part.interleave, r = p.part.rank;
+      if (cur.b != mask_b) {
+        mask_b = cur.b;
+        mask_from = dcp_local_len((int64_t)cur.Lg - (QB - 1), N, I, r);
+      }
+      const int64_t j0 = (int64_t)cur.t * kTile;
+      if (j0 + kTile > mask_from) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t g = dcp_global_index(j0 + 4 * q4 + j, N, I, r);
+#pragma unroll
+          for (int c = 0; c < QB; ++c)
+            if (g > (int64_t)cur.Lg - QB + c) x[c][j] = -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax (base 2) per query token; lane: head l16, tokens 4 q4 + j.  A
+    // row that has seen no token yet keeps m = -inf with no NaN.
+    bf16x4 pb[QB];
+    bool moved = false;
+    float alpha[QB];
+#pragma unroll
+    for (int c = 0; c < QB; ++c) {
+      float mloc = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
+      mloc = max_over_groups(mloc);
+      const float m_new = mloc > m_run[c] + kRescaleSlack ? mloc : m_run[c];
+      const bool none = m_new == -INFINITY;
+      alpha[c] = none ? 1.f : fast_exp2(m_run[c] - m_new);
+      float lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pr = none ? 0.f : fast_exp2(x[c][j] - m_new);
+        lsum += pr;
+        pb[c][j] = (__bf16)pr;
+      }
+      lsum = sum_over_groups(lsum);
+      l_run[c] = l_run[c] * alpha[c] + lsum;
+      moved = moved || m_new != m_run[c];
+      m_run[c] = m_new;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int c = 0; c < QB; ++c)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) oacc[c][m] *= alpha[c];
+    }
+
+    // ---- O^T [128 dims x 16 heads] += V^T [128 x 16 tokens] P^T [16 x 16]; a V^T
+    // operand serves all QB
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const bf16x4 va_m = __builtin_bit_cast(bf16x4, lds_read_tr16(vb + va[m]));
+#pragma unroll
+      for (int c = 0; c < QB; ++c) oacc[c][m] = mfma16x16x16(va_m, pb[c], oacc[c][m]);
+    }
 
     // ---- end of a request piece: normalisation and destination; stored after the
     // next barrier
@@ -303,15 +379,18 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       const bool whole = piece_t0 == 0 && last_of_req;
       const int64_t slot = 2 * w + (first_piece ? 0 : 1);
       pend = true;
-      // a row that saw no token of the piece: O = 0, LSE = -inf
-      pend_inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-      pend_lse = l_run > 0.f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
-      pend_o = (whole ? p.out_o + ((int64_t)cur.b * p.out_req_rows + head) * kD : p.ws_o + (slot * H + head) * kD) + 4 * q4;
-      pend_l = whole ? p.out_lse + (int64_t)cur.b * p.out_req_rows + head : p.ws_lse + slot * H + head;
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        // a row that saw no token of the piece: O = 0, LSE = -inf
+        pend_inv[c] = l_run[c] > 0.f ? 1.0f / l_run[c] : 0.f;
+        pend_lse[c] = l_run[c] > 0.f ? (m_run[c] + fast_log2(l_run[c])) * kLn2 : -INFINITY;
+        m_run[c] = -INFINITY;
+        l_run[c] = 0.f;
+      }
+      pend_o = (whole ? p.out_o + ((int64_t)cur.b * p.out_req_rows + head) * kD : p.ws_o + (slot * rows + head) * kD) + 4 * q4;
+      pend_l = whole ? p.out_lse + (int64_t)cur.b * p.out_req_rows + head : p.ws_lse + slot * rows + head;
       piece_t0 = 0;
       first_piece = false;
-      m_run = -INFINITY;
-      l_run = 0.f;
     }
     advance_loader();
   }
@@ -323,12 +402,23 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
 
 }  // namespace gqa
 
-hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream) {
+namespace {
+template <int QB>
+void launch_gqa_qb(const PartialParams& p, hipStream_t stream) {
   const int grid = p.part.num_parts * p.num_head_groups;
   switch (gqa_kv_heads_per_group(p.num_kv_heads)) {
-    case 4: hipLaunchKernelGGL(gqa::gqa_partial_kernel<4>, dim3(grid), dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(gqa::gqa_partial_kernel<2>, dim3(grid), dim3(128), 0, stream, p); break;
-    default: hipLaunchKernelGGL(gqa::gqa_partial_kernel<1>, dim3(grid), dim3(64), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((gqa::gqa_partial_kernel<4, QB>), dim3(grid), dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((gqa::gqa_partial_kernel<2, QB>), dim3(grid), dim3(128), 0, stream, p); break;
+    default: hipLaunchKernelGGL((gqa::gqa_partial_kernel<1, QB>), dim3(grid), dim3(64), 0, stream, p); break;
+  }
+}
+}  // namespace
+
+hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream) {
+  switch (p.q_block) {
+    case 1: launch_gqa_qb<1>(p, stream); break;
+    case 2: launch_gqa_qb<2>(p, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

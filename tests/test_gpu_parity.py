@@ -629,10 +629,13 @@ MTP_CASES = [
     ("mla_tiny", 3, dict(dcp_size=4, interleave=2, lengths=(7, 9, 2049, 64))),
     ("mla_long_b128", 2, dict(batch=3, lengths=(5000, 20000, 1030))),
     ("mla_long_b128", 4, dict(batch=2, lengths=(3000, 1025))),
-    # GQA: one single-token pass per query token, each over its causal length
+    # GQA: passes of two query tokens (and one for an odd count), each pass's tokens on
+    # two MFMA column blocks over the newest token's causal length
     ("gqa_b32", 2, dict(lengths=(5000, 1, 2, 33))),
     ("gqa_b32", 3, dict(dcp_size=2, interleave=3, block_size=32, lengths=(1000, 37, 2, 3, 4))),
     ("gqa_b32", 4, dict(num_q_heads=32, num_kv_heads=8, dcp_size=3, interleave=16, lengths=(2049, 700))),
+    ("gqa_b32", 5, dict(num_q_heads=16, num_kv_heads=2, dcp_size=2, interleave=4, block_size=16,
+                        lengths=(300, 5, 6, 7, 129))),
 ]
 
 
@@ -679,7 +682,9 @@ def test_mtp_single_query_is_the_decode_call(name):
     ("mla_tiny", 4, dict(dcp_size=3, interleave=5, block_size=32, lengths=(1000, 3000, 1, 2, 3, 17))),
     ("mla_tiny", 2, dict(dcp_size=2, interleave=1, lengths=(64, 65))),
     ("gqa_b32", 3, dict(dcp_size=3, interleave=5, block_size=32, lengths=(1000, 3000, 1, 2, 3, 17))),
-    ("gqa_b32", 2, dict(dcp_size=2, interleave=1, lengths=(16, 17, 33)))])
+    ("gqa_b32", 2, dict(dcp_size=2, interleave=1, lengths=(16, 17, 33))),
+    ("gqa_b32", 5, dict(num_q_heads=16, num_kv_heads=2, dcp_size=4, interleave=3, block_size=16,
+                        lengths=(200, 4, 5, 6, 31)))])
 def test_mtp_census(name, q_len, kw):
     """q = 0 and V rows = bits of the global token id: for every query, O * count recovers
     exactly how many of the tokens it may see (the rank's tokens at positions
