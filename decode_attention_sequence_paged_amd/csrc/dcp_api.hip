@@ -20,7 +20,7 @@ constexpr int32_t kMaxParts = 1 << 16;
 constexpr int32_t kMaxMlaRows = 512;  // MLA score rows (query tokens x heads) per request
 constexpr int64_t kMaxMtpRows = kMaxMlaRows;
 constexpr int32_t kMaxGqaQueryTokens = 64;  // query tokens per request of a GQA multi-token call
-constexpr int32_t kGqaMaxQueryBlock = 2;    // query tokens per GQA pass (MFMA column blocks)
+constexpr int32_t kGqaMaxQueryBlock = 4;    // query tokens per GQA pass (MFMA column blocks)
 constexpr int32_t kMaxDevices = 64;
 
 // Cache of the compute-unit count per device (filled on first use; concurrent callers
@@ -113,7 +113,7 @@ WsLayout ws_layout(int32_t batch, int32_t parts, int32_t heads, int32_t v_dim) {
 }
 
 // Multi-token decode queries.  MLA: q_len query tokens of num_q_heads heads become
-// q_len * num_q_heads score rows of one pass.  GQA: passes of up to two query tokens
+// q_len * num_q_heads score rows of one pass.  GQA: passes of up to four query tokens
 // (the kernel keeps a KV head's query heads on the 16 MFMA columns, one column block
 // per query token), so the head shapes are those of a single-token call and the
 // workspace holds the pieces of one pass.
@@ -355,7 +355,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
     return hip_status(dcp::launch_split_reduce(r, s));
   }
   // GQA: query token i of a request at global length L sees the positions <= L - q_len
-  // + i.  Passes of qb = 2 or 1 consecutive query tokens i0 .. i0 + qb - 1: the
+  // + i.  Passes of qb = 4, 2 or 1 consecutive query tokens i0 .. i0 + qb - 1: the
   // partition covers the pass's newest token's positions (length L - (q_len - i0 - qb))
   // and the kernel masks, for each older token, the newest positions it may not see.
   // Each pass has its own slices of q [B, q_len, H, D] and of the outputs
@@ -366,7 +366,7 @@ dcp_status_t dcp_decode_partial_mtp(const dcp_attn_desc_t* desc, int32_t q_len, 
   r.out_req_rows = p.out_req_rows;
   for (int32_t i0 = 0; i0 < q_len;) {
     const int32_t left = q_len - i0;
-    const int32_t qb = left >= kGqaMaxQueryBlock ? kGqaMaxQueryBlock : 1;
+    const int32_t qb = left >= 4 ? 4 : (left >= 2 ? 2 : 1);
     p.q_block = qb;
     p.part.len_offset = q_len - i0 - qb;
     // a request's query slices and output rows grow with the pass's query tokens

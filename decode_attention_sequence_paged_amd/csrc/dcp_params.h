@@ -29,7 +29,7 @@ struct PartialParams {
   int32_t num_head_groups;  // work-groups sharing one span (disjoint head sets)
   int32_t q_len;            // query tokens per request (1: single-token decode)
   int32_t heads_per_token;  // query heads per query token; rows = q_len * heads_per_token
-  int32_t q_block;          // GQA: query tokens of this pass (1 or 2), on consecutive MFMA
+  int32_t q_block;          // GQA: query tokens of this pass (1, 2 or 4), on consecutive MFMA
                             // column blocks; its pieces have q_block * num_q_heads rows
   float scale_log2;         // softmax_scale * log2(e)
   PartitionArgs part;

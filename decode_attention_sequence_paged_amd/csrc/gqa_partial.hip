@@ -30,12 +30,10 @@
 //  * Rows of a request's partial last tile past its end are copied from the page
 //    (always inside the pool) and made inert: scores -inf, V part zeroed in LDS.
 //    Finished pieces are stored after the next barrier, ahead of the next copies.
-//  * Multi-token decode queries (blog Sec. 6): QB query tokens of a request (QB = 1 or
-//    2) go on QB consecutive MFMA column blocks of the same KV head, so a pass streams
-//    the pages once for both: every K and V^T operand read feeds QB MFMAs.  (Four
-//    tokens per pass need more than 256 VGPRs; the compiler then parks values in
-//    accumulation registers, and with the query slices loaded by inline asm it could
-//    move a slice register before its load has landed, so passes stop at two.)  Query token i sees the global positions <= L - q_len + i; the pass's
+//  * Multi-token decode queries (blog Sec. 6): QB query tokens of a request (QB = 1, 2
+//    or 4) go on QB consecutive MFMA column blocks of the same KV head, so a pass
+//    streams the pages once for all of them: every K and V^T operand read feeds QB
+//    MFMAs.  Query token i sees the global positions <= L - q_len + i; the pass's
 //    partition covers its newest token's positions and the older tokens' columns
 //    mask the few newest positions they may not see.
 #include "dcp_device.h"
@@ -76,7 +74,7 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 template <int KVW, int QB>
 __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams p) {
-  static_assert(QB == 1 || QB == 2, "query tokens per pass");
+  static_assert(QB == 1 || QB == 2 || QB == 4, "query tokens per pass");
   using C = Cfg<KVW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::kStages * C::kStageBytes];
   __shared__ int64_t s_scan[C::kThreads];
@@ -183,20 +181,30 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
   // Column block c holds query token c of the pass (its slice QB * ... apart: the
   // tokens of a request are consecutive in q).
   bf16x8 qreg[QB][4], qnext[QB][4];
+  // With four tokens the kernel needs more than 256 VGPRs and the compiler parks values
+  // in accumulation registers: the slices are then ordinary loads, which the compiler
+  // tracks (it waits for them, and for the copies issued after them, before their first
+  // use, i.e. once per request), so no register can be moved before its load has landed.
   auto load_q = [&](bf16x8 (&dst)[QB][4], int b) {
 #pragma unroll
     for (int c = 0; c < QB; ++c) {
       const uint16_t* qp = p.q + (int64_t)b * p.q_req_stride + ((int64_t)c * H + head) * kD + 8 * q4;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[c][s]) : "v"(qp), "n"(64 * s) : "memory");
+      for (int s = 0; s < 4; ++s) {
+        if constexpr (QB == 4)
+          dst[c][s] = *(const bf16x8*)(qp + 32 * s);
+        else
+          asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(dst[c][s]) : "v"(qp), "n"(64 * s) : "memory");
+      }
     }
   };
   auto settle = [&](bf16x8 (&r)[QB][4]) {
+    if constexpr (QB != 4) {
 #pragma unroll
-    for (int c = 0; c < QB; ++c)
+      for (int c = 0; c < QB; ++c)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(r[c][s]));
+        for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(r[c][s]));
+    }
   };
 
   f32x4 oacc[QB][8];
@@ -418,6 +426,7 @@ hipError_t launch_gqa_partial(const PartialParams& p, hipStream_t stream) {
   switch (p.q_block) {
     case 1: launch_gqa_qb<1>(p, stream); break;
     case 2: launch_gqa_qb<2>(p, stream); break;
+    case 4: launch_gqa_qb<4>(p, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
