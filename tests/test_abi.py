@@ -179,11 +179,11 @@ def test_mtp_entry_point_validation():
     assert dcp.dcp_decode_workspace_size_mtp(mla, 4, 4, 8) > dcp.dcp_decode_workspace_size(mla, 4, 8)
     assert dcp.dcp_decode_workspace_size_mtp(mla, 0, 4, 8) == 0
     assert dcp.dcp_decode_workspace_size_mtp(mla, 9, 4, 8) == 0      # 9 x 64 rows > 512
-    # GQA: passes of up to two query tokens, so the pieces of one two-token pass
+    # GQA: passes of up to four query tokens, so the pieces of one four-token pass
     one = dcp.dcp_decode_workspace_size(gqa, 4, 8)
-    assert dcp.dcp_decode_workspace_size_mtp(gqa, 1, 4, 8) == one > 0
-    assert dcp.dcp_decode_workspace_size_mtp(gqa, 2, 4, 8) > one
-    assert dcp.dcp_decode_workspace_size_mtp(gqa, 64, 4, 8) == dcp.dcp_decode_workspace_size_mtp(gqa, 2, 4, 8)
+    size = lambda q_len: dcp.dcp_decode_workspace_size_mtp(gqa, q_len, 4, 8)
+    assert size(1) == one > 0
+    assert size(64) == size(4) > size(2) > one
     assert dcp.dcp_decode_workspace_size_mtp(gqa, 65, 4, 8) == 0
     fake = 1 << 20
     def call(desc=mla, q_len=2, B=2, rank=0):
