@@ -344,8 +344,9 @@ def run_next(args):
                                                            gw.interleave, ws, o, lse))
                for grc in grcs]
         t = float(np.median(_event_ms_calls(fns, args.steps, args.warmup)))
-        gmtp.append({"q_len": q_len, "passes": (q_len + 1) // 2, "call_ms_median": round(t, 4),
-                     "kv_gbps_per_query_token": round(gkv * q_len / (t * 1e-3) / 1e9, 1),
+        passes = q_len // 4 + (q_len % 4) // 2 + q_len % 2  # of 4, 2 and 1 query tokens
+        gmtp.append({"q_len": q_len, "passes": passes, "call_ms_median": round(t, 4),
+                     "kv_gbps": round(gkv * passes / (t * 1e-3) / 1e9, 1),
                      "ms_per_query_token": round(t / q_len, 4)})
         del q, ws, o, lse, fns
     out["gqa_multi_token_queries"] = {"workload": describe(gw), "ranks": gw.dcp_size, "rows": gmtp}
