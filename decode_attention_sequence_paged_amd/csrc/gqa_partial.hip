@@ -255,6 +255,10 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
 
   // ---- prologue: query slice and the first kStages-1 tiles
   load_q(qreg, cc.b);
+  // Compiler-tracked slices (QB = 4) must not reach the loop still pending: the wait
+  // counting, blind to the asm copies issued after them, would otherwise keep a wait for
+  // them in front of every tile's MFMAs, draining the copy ring each tile.
+  if constexpr (QB == 4) wait_vmcnt_builtin<0>();
   next_src();
 #pragma unroll
   for (int t = 0; t < C::kStages - 1; ++t) {
