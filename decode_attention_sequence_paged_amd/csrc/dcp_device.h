@@ -322,16 +322,27 @@ __device__ __forceinline__ float sum_over_groups(float x) {
 // Causal mask of multi-token decode queries: the q_len queries are the request's last
 // q_len positions, and query i (score row `row`, i = row / heads_per_token) sees the
 // global positions <= Lg - q_len + i.  Masks this lane's eight scores (tokens 4 q4 + e
-// and 16 + 4 q4 + e of the tile at cursor `cur`); tiles whose last token every query
-// sees are left alone after one wave-uniform test.
+// and 16 + 4 q4 + e of the tile at cursor `cur`).  The local tokens every query sees
+// (global position <= Lg - q_len) are the first dcp_local_len(Lg - q_len + 1) of the
+// request; that count is computed once per request (CausalFrom), so a tile before it is
+// left alone after one wave-uniform compare.
+struct CausalFrom {
+  int b = -1;
+  int64_t from = 0;  // local tokens of request b that every query sees
+};
+
 __device__ __forceinline__ void causal_mask(const PartialParams& p, const Cursor& cur, int nvalid,
-                                            int row, int q4, f32x4& s0, f32x4& s1) {
+                                            int row, int q4, f32x4& s0, f32x4& s1, CausalFrom& cf) {
   if (p.q_len <= 1) return;
   const int N = p.part.num_ranks, I = p.part.interleave, r = p.part.rank;
+  const int64_t lim0 = (int64_t)cur.Lg - p.q_len;
+  if (cur.b != cf.b) {
+    cf.b = cur.b;
+    cf.from = dcp_local_len(lim0 + 1, N, I, r);
+  }
   const int64_t j0 = (int64_t)cur.t * kTileTokens;
   const int64_t last = j0 + (nvalid < kTileTokens ? nvalid : kTileTokens) - 1;
-  const int64_t lim0 = (int64_t)cur.Lg - p.q_len;
-  if (dcp_global_index(last, N, I, r) <= lim0) return;
+  if (last < cf.from) return;
   const int64_t lim = lim0 + row / p.heads_per_token;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {

@@ -253,6 +253,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   // of the tile as the B operand of its P.V.
   float m_run = -INFINITY;
   float l_run = 0.f;
+  CausalFrom cfrom;
   bf16x8 pb;
   float alpha = 1.f;
   bool moved = false;
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
         if (16 + 4 * q4 + j >= nvalid) s1[j] = -INFINITY;
       }
     }
-    causal_mask(p, cur, nvalid, head, q4, s0, s1);
+    causal_mask(p, cur, nvalid, head, q4, s0, s1, cfrom);
     softmax(s0, s1);
     if (__any(moved)) {
 #pragma unroll
@@ -597,6 +598,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
     };
 
     float m_run = -INFINITY, l_run = 0.f;
+    CausalFrom cfrom;
     Cursor sc = cur0;
     Piece pc{sc.t, true};
     bool q_pending = true;
@@ -628,7 +630,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
           if (16 + 4 * q4 + e >= nvalid) s1[e] = -INFINITY;
         }
       }
-      causal_mask(p, cur, nvalid, head, q4, s0, s1);
+      causal_mask(p, cur, nvalid, head, q4, s0, s1, cfrom);
       // Online softmax over the tile's 32 scores of this lane's head (lazy rescale).  The
       // running maximum m_run (equal in the head's four lanes) moves only when a score
       // exceeds it by more than kRescaleSlack, which each lane can test on its own 8 scores:
