@@ -325,7 +325,7 @@ def run_next(args):
     del rcs
     torch.cuda.empty_cache()
 
-    # GQA multi-token queries (passes of two query tokens on two MFMA column blocks)
+    # GQA multi-token queries (passes of up to four query tokens on as many MFMA column blocks)
     gw = di.WORKLOADS["gqa_b32"]
     gdesc = paged.desc_for(gw)
     gsl = torch.tensor(np.asarray(gw.lengths, dtype=np.int32), device="cuda")

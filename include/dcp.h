@@ -239,8 +239,9 @@ dcp_status_t dcp_decode_partial_noalloc(const dcp_attn_desc_t* desc, const void*
  * Every other argument as for dcp_decode_partial.
  * Supported: MLA with q_len * H <= 512, computed in one pass with the q_len * H
  * (query token, head) pairs as score rows; GQA with q_len <= 64, computed in passes
- * of two consecutive query tokens (one for an odd last token), each pass reading the
- * rank's pages of its newer token's causal length once for both tokens.
+ * of four consecutive query tokens (then two, then one for what is left), each pass
+ * reading the rank's pages of its newest token's causal length once for all its
+ * tokens.
  * Errors: INVALID_VALUE (q_len < 1, and as dcp_decode_partial), NOT_SUPPORTED,
  * WORKSPACE (nothing runs on these), HIP (a GQA call that fails to launch pass i
  * leaves passes 0 .. i-1 enqueued).                                            */

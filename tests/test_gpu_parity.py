@@ -629,13 +629,15 @@ MTP_CASES = [
     ("mla_tiny", 3, dict(dcp_size=4, interleave=2, lengths=(7, 9, 2049, 64))),
     ("mla_long_b128", 2, dict(batch=3, lengths=(5000, 20000, 1030))),
     ("mla_long_b128", 4, dict(batch=2, lengths=(3000, 1025))),
-    # GQA: passes of two query tokens (and one for an odd count), each pass's tokens on
-    # two MFMA column blocks over the newest token's causal length
+    # GQA: passes of four query tokens, then two, then one for what is left, each pass's
+    # tokens on that many MFMA column blocks over its newest token's causal length
     ("gqa_b32", 2, dict(lengths=(5000, 1, 2, 33))),
     ("gqa_b32", 3, dict(dcp_size=2, interleave=3, block_size=32, lengths=(1000, 37, 2, 3, 4))),
     ("gqa_b32", 4, dict(num_q_heads=32, num_kv_heads=8, dcp_size=3, interleave=16, lengths=(2049, 700))),
     ("gqa_b32", 5, dict(num_q_heads=16, num_kv_heads=2, dcp_size=2, interleave=4, block_size=16,
                         lengths=(300, 5, 6, 7, 129))),
+    ("gqa_b32", 7, dict(num_q_heads=64, num_kv_heads=8, dcp_size=3, interleave=2, block_size=64,
+                        lengths=(1500, 6, 7, 8, 9, 65))),
 ]
 
 
