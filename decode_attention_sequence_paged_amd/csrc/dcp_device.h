@@ -1,5 +1,6 @@
 // Device-side helpers shared by the decode-attention kernels (gfx950 / CDNA4).
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,6 +83,52 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Softmax weights as MFMA operands.  A bf16 operand keeps 8 significant bits, so a
+// weight rounded to bf16 moves by up to 2^-8 of itself; when a few tokens carry most
+// of a row's weight (a short request) that reaches the output as up to about
+// 2^-8 |V|, close to the 5e-3 accuracy bound.  The P.V products therefore take P as
+// two bf16 operands accumulated into the same O, hi = bf16(P) and lo = P - hi
+// (|lo| <= 2^-8 P), so that the weights enter with about 16 significant bits.  The
+// row sum l is accumulated from the fp32 P.
+//
+// The low parts only matter for weights that end up a sizeable share of their row.
+// A tile takes them if its request has at most kLowAllTokens local tokens, or if some
+// weight in it exceeds kLowShare of its row's running sum (every first tile of a
+// piece, and later tiles that hold a dominant token).  The weights of the other
+// tiles are each below kLowShare of the row's final sum and spread over more than
+// kLowAllTokens tokens, so their bf16 rounding errors average out (below about 7e-4
+// with 64 heads of 512 dims).  In long rows few tiles qualify, so the extra MFMAs
+// cost little there.
+constexpr float kLowShare = 0.25f;
+constexpr int kLowAllTokens = 256;
+__device__ __forceinline__ __bf16 bf16_low_part(float x, __bf16 hi) { return (__bf16)(x - (float)hi); }
+
+// Low parts handed from one wave to another through LDS are coded compactly, as fp8
+// (OCP e4m3: 4 significant bits, finite up to 448) of lo * 2^8.  P <= 2^8 (the lazy
+// rescale's slack) keeps the code at most 2^8; a lo below 2^-18 (a weight below about
+// 2^-10 of the row maximum) codes to 0 and leaves that weight at bf16 precision.
+// Eight codes per lane: codes 2k and 2k+1 in 16-bit half k % 2 of word k / 2; the
+// decode multiplies by 2^-8 on its way to bf16.
+constexpr float kLowScale = 256.f;
+__device__ __forceinline__ u32x2 code_low_parts(const float lo[8]) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[0] * kLowScale, lo[1] * kLowScale, 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2] * kLowScale, lo[3] * kLowScale, w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[4] * kLowScale, lo[5] * kLowScale, 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[6] * kLowScale, lo[7] * kLowScale, w1, true);
+  return u32x2{(unsigned)w0, (unsigned)w1};
+}
+__device__ __forceinline__ bf16x8 decode_low_parts(u32x2 w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  constexpr float kInv = 1.f / kLowScale;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], kInv, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[0], kInv, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], kInv, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[1], kInv, true);
+  // moved as whole dwords (see join_tr16)
+  return __builtin_bit_cast(bf16x8, u32x4{__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b),
+                                          __builtin_bit_cast(unsigned, c), __builtin_bit_cast(unsigned, d)});
 }
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -36,6 +36,9 @@
 //    MFMAs.  Query token i sees the global positions <= L - q_len + i; the pass's
 //    partition covers its newest token's positions and the older tokens' columns
 //    mask the few newest positions they may not see.
+//  * P enters the P.V MFMAs as its bf16 high part and, in the tiles where a weight is
+//    a sizeable share of its row, also as its bf16 low part (bf16_low_part in
+//    dcp_device.h).
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -346,8 +349,9 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
 
     // ---- online softmax (base 2) per query token; lane: head l16, tokens 4 q4 + j.  A
     // row that has seen no token yet keeps m = -inf with no NaN.
-    bf16x4 pb[QB];
+    bf16x4 pb[QB], pl[QB];  // P's high and low bf16 parts (see bf16_low_part)
     bool moved = false;
+    bool big = false;  // some weight is more than kLowShare of its row's running sum
     float alpha[QB];
 #pragma unroll
     for (int c = 0; c < QB; ++c) {
@@ -367,6 +371,7 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
       l_run[c] = l_run[c] * alpha[c] + lsum;
       moved = moved || m_new != m_run[c];
       m_run[c] = m_new;
+      big = big || (!none && fast_exp2(mloc - m_new) > kLowShare * l_run[c]);
     }
     if (__any(moved)) {
 #pragma unroll
@@ -377,11 +382,23 @@ __global__ __launch_bounds__(64 * KVW, 1) void gqa_partial_kernel(PartialParams 
 
     // ---- O^T [128 dims x 16 heads] += V^T [128 x 16 tokens] P^T [16 x 16]; a V^T
     // operand serves all QB
+    bf16x4 vam[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const bf16x4 va_m = __builtin_bit_cast(bf16x4, lds_read_tr16(vb + va[m]));
+      vam[m] = __builtin_bit_cast(bf16x4, lds_read_tr16(vb + va[m]));
 #pragma unroll
-      for (int c = 0; c < QB; ++c) oacc[c][m] = mfma16x16x16(va_m, pb[c], oacc[c][m]);
+      for (int c = 0; c < QB; ++c) oacc[c][m] = mfma16x16x16(vam[m], pb[c], oacc[c][m]);
+    }
+    // with the low parts of the weights in a tile that needs them (see kLowShare)
+    if (cur.Lr <= kLowAllTokens || __any(big)) {
+#pragma unroll
+      for (int c = 0; c < QB; ++c) {
+        const bool none = m_run[c] == -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pl[c][j] = bf16_low_part(none ? 0.f : fast_exp2(x[c][j] - m_run[c]), pb[c][j]);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) oacc[c][m] = mfma16x16x16(vam[m], pl[c], oacc[c][m]);
+      }
     }
 
     // ---- end of a request piece: normalisation and destination; stored after the

@@ -38,6 +38,9 @@
 //    kRescaleSlack (log2 units), so the 128-register O accumulator is rarely
 //    rescaled; P stays <= 2^kRescaleSlack and the final LSE uses the same maximum,
 //    so the result is unchanged.
+//  * P enters the P.V MFMAs as its bf16 high part and, in the tiles where a weight is
+//    a sizeable share of its row, also as its bf16 low part (bf16_low_part in
+//    dcp_device.h), so that short requests keep about 16 bits of every weight.
 #include "dcp_device.h"
 #include "dcp_internal.h"
 
@@ -254,12 +257,13 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   float m_run = -INFINITY;
   float l_run = 0.f;
   CausalFrom cfrom;
-  bf16x8 pb;
+  bf16x8 pb, pl;  // P's high and low bf16 parts (see bf16_low_part)
   float alpha = 1.f;
   bool moved = false;
+  bool need_lo = false;  // the tile takes the low parts (see kLowShare)
   // Softmax over the tile's 32 scores of this lane's head (x[0..3]: tokens 4 q4 + j,
   // x[4..7]: tokens 16 + 4 q4 + j).
-  auto softmax = [&](const f32x4& s0, const f32x4& s1) {
+  auto softmax = [&](const f32x4& s0, const f32x4& s1, bool all_lo) {
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) { x[j] = s0[j]; x[j + 4] = s1[j]; }
@@ -281,6 +285,12 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
     lsum = sum_over_groups(lsum);
     l_run = l_run * alpha + lsum;
     m_run = m_new;
+    // mloc is the row's maximum over the tile
+    need_lo = all_lo || __any(!none && fast_exp2(mloc - m_new) > kLowShare * l_run);
+    if (need_lo) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pl[j] = bf16_low_part(none ? 0.f : fast_exp2(x[j] - m_new), pb[j]);
+    }
   };
 
   f32x4 oacc[kVBlocks];
@@ -293,7 +303,8 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
   // the source is its place in the instruction stream.  Source lane l16 of each
   // 16-lane group addresses row 4 q4 + l16 / 4 (and +16); lane i then holds dim
   // 16 m + i of the tokens P's element j stands for.
-  auto pv = [&](const DCP_LDS uint8_t* tb, int stage) {
+  auto pv = [&](const DCP_LDS uint8_t* tb, int stage, auto lo_tag) {
+    constexpr bool kLo = decltype(lo_tag)::value;
     u32x2 v1[kPrefetchV], v2[kPrefetchV];
 #pragma unroll
     for (int m = 0; m < kPrefetchV; ++m) {
@@ -312,6 +323,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
       for (int k = 0; k < C::kCopies; ++k)
         if (k * kVBlocks / C::kCopies == m) issue_copy(k, stage);
       oacc[m] = mfma16x16x32(a, pb, oacc[m]);
+      if constexpr (kLo) oacc[m] = mfma16x16x32(a, pl, oacc[m]);
     }
   };
 
@@ -413,12 +425,13 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
       }
     }
     causal_mask(p, cur, nvalid, head, q4, s0, s1, cfrom);
-    softmax(s0, s1);
+    softmax(s0, s1, cur.Lr <= kLowAllTokens);
     if (__any(moved)) {
 #pragma unroll
       for (int m = 0; m < kVBlocks; ++m) oacc[m] *= alpha;
     }
-    pv(tb, issued % kStages);
+    if (need_lo) pv(tb, issued % kStages, std::true_type{});
+    else pv(tb, issued % kStages, std::false_type{});
     ++issued;
 
     // ---- end of a request piece: its normalisation and destination; the stores
@@ -454,10 +467,13 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
 //    It computes S^T of tile j+1 (16x16x32 MFMA, four accumulation chains: token
 //    block x k-step parity), runs the online softmax and leaves P^T (bf16, laid out
 //    as the MFMA B operand), the rescale factor of each head and, at the end of a
-//    piece, 1/l in LDS; it stores the piece's LSE itself.
+//    piece, 1/l in LDS; it stores the piece's LSE itself.  In a tile where its head
+//    block needs them it also leaves the low parts of P (fp8-coded), and says so in
+//    the sign of the block's rescale factors.
 //  * P.V waves 4..11: wave v owns output dims 64 v .. 64 v + 63 of all 64 heads
 //    (16 O^T accumulators of 16 dims x 16 heads).  During tile j's interval it
-//    rescales, accumulates O^T += V^T P^T for tile j and stores finished pieces;
+//    rescales, accumulates O^T += V^T P^T for tile j (a second pass adds the low
+//    parts of the head blocks that left them) and stores finished pieces;
 //    the first four also issue the copies of tile j+3 into the stage tile j-1 has
 //    just released.
 // Each role therefore keeps the matrix pipe busy while the other waits on a
@@ -496,6 +512,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
   constexpr int kDimBlocks = PVC::kDimBlocks;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kTileBytes];
   __shared__ __attribute__((aligned(16))) bf16x8 s_p[2][kHeadBlocks][64];  // [tile parity][head block][lane]
+  __shared__ __attribute__((aligned(16))) u32x2 s_pl[2][kHeadBlocks][64];   // the low parts, fp8-coded
   __shared__ __attribute__((aligned(16))) float s_alpha[2][16][kHeadBlocks];  // [parity][head in block][block]
   __shared__ __attribute__((aligned(16))) float s_inv[2][16][kHeadBlocks];
   __shared__ int64_t s_loc[4];
@@ -660,11 +677,21 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
         pb[e] = (__bf16)pr;
       }
       s_p[par][sb][lane] = pb;
-      if (q4 == 0) s_alpha[par][l16][sb] = alpha;
+      // the head block's tile takes the low parts of its weights (see kLowShare); the
+      // P.V waves read that from the sign of the block's rescale factors
+      const float l_tot = sum_over_groups(l_run);
+      const float pmax = none ? 0.f : fast_exp2(mloc - m_run);
+      const bool need_lo = cur.Lr <= kLowAllTokens || __any(pmax > kLowShare * l_tot);
+      if (need_lo) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = (none ? 0.f : fast_exp2(x[e] - m_run)) - (float)pb[e];
+        s_pl[par][sb][lane] = code_low_parts(lo);
+      }
+      if (q4 == 0) s_alpha[par][l16][sb] = need_lo ? -alpha : alpha;
       if (cur.t == cur.ntile - 1 || j == total - 1) {
         bool whole;
         const int64_t row = piece_row(pc, cur, head_ok ? head : 0, whole);
-        const float l_tot = sum_over_groups(l_run);
         if (q4 == 0) {
           // a row that saw no token of the piece: O = 0, LSE = -inf
           s_inv[par][l16][sb] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
@@ -796,7 +823,12 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
           for (int e = lane; e < n; e += 64)
             zero_lds16(lds_addr(tb + (nvalid + e / kC) * kRowBytes + (kC * v + e % kC) * 16));
         }
-        const f32x4 alpha = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
+        // rescale factors of the four head blocks; a set sign bit asks for the low parts
+        const f32x4 araw = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
+        const u32x4 abits = __builtin_bit_cast(u32x4, araw);
+        const int lo_blocks = uniform((int)((abits[0] >> 31) | (abits[1] >> 31) << 1 | (abits[2] >> 31) << 2 |
+                                            (abits[3] >> 31) << 3));
+        const f32x4 alpha = __builtin_bit_cast(f32x4, abits & 0x7FFFFFFFu);
         bf16x8 pP[kHeadBlocks];
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocks; ++hb) pP[hb] = s_p[par][hb][lane];
@@ -807,6 +839,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
 #pragma unroll
             for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[m][hb] *= alpha[hb];
         }
+        // O^T += V^T P^T over the tile with the high parts of the weights
         u32x2 v1[kPfV], v2[kPfV];
 #pragma unroll
         for (int m = 0; m < kPfV; ++m) {
@@ -833,6 +866,25 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kHeadBlocks * (kDimBlocks < kPfV ? kDimBlocks : kPfV), 0);
+        if (lo_blocks) {
+          // and with the low parts of the head blocks whose tile needs them: a second
+          // pass over the V^T operands (kept apart so the common pass above keeps its
+          // registers)
+          u32x2 w1[kDimBlocks], w2[kDimBlocks];
+#pragma unroll
+          for (int m = 0; m < kDimBlocks; ++m) {
+            w1[m] = lds_read_tr16(tb + voff(m));
+            w2[m] = lds_read_tr16(tb + voff(m) + 16 * kRowBytes);
+          }
+#pragma unroll
+          for (int hb = 0; hb < kHeadBlocks; ++hb) {
+            if (lo_blocks >> hb & 1) {
+              const bf16x8 pL = decode_low_parts(s_pl[par][hb][lane]);
+#pragma unroll
+              for (int m = 0; m < kDimBlocks; ++m) oacc[m][hb] = mfma16x16x32(join_tr16(w1[m], w2[m]), pL, oacc[m][hb]);
+            }
+          }
+        }
         if (cur.t == cur.ntile - 1 || i == total - 1) {
           // 1/l of every head leaves LDS now: the next tile of this parity overwrites it
           pend_inv = *(const DCP_LDS f32x4*)&s_inv[par][l16][0];

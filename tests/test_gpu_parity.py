@@ -50,7 +50,7 @@ def run_rank(wl, rank, census=False, parts=0, q=None, lengths=None):
     return o, lse, rc
 
 
-def check_close(o_gpu, lse_gpu, o_ref, lse_ref, what):
+def check_close(o_gpu, lse_gpu, o_ref, lse_ref, what, tol_o=TOL_O):
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
     empty = np.isneginf(lse_ref)
@@ -63,7 +63,7 @@ def check_close(o_gpu, lse_gpu, o_ref, lse_ref, what):
         dl = np.abs(lse_gpu[full] - lse_ref[full]).max()
         print("%s: max|dO|=%.3g max|dLSE|=%.3g" % (what, do, dl), flush=True)
         assert np.all(np.isfinite(o_gpu[full])), what + ": non-finite O"
-        assert do <= TOL_O, "%s: max|dO| = %g" % (what, do)
+        assert do <= tol_o, "%s: max|dO| = %g" % (what, do)
         assert dl <= TOL_LSE, "%s: max|dLSE| = %g" % (what, dl)
 
 
@@ -776,6 +776,36 @@ def test_random_shapes_every_rank_and_merge(seed):
         else:
             o_ref, l_ref = oracle.mtp_full_attention(wl, b, q_len)
         check_close(om[b], lm[b], o_ref, l_ref, "random %d merged b=%d" % (seed, b))
+
+
+@pytest.mark.parametrize("kind,heads,q_len", [("mla", 64, 1), ("mla", 128, 1), ("mla", 16, 1), ("mla", 32, 2),
+                                               ("gqa", 64, 1), ("gqa", 64, 2), ("gqa", 64, 5)])
+def test_short_requests_weight_precision(kind, heads, q_len):
+    """Requests of 1 to 40 tokens, where a few tokens carry most of each row's softmax
+    weight.  Weights rounded to bf16 alone move O by up to about 2^-8 |V| (4-5e-3 over
+    rows like these, next to the 5e-3 bound); with the weights taken as high and low
+    bf16 parts the kernels stay below 1e-3 here (about 2e-4 expected), which this
+    test requires of every row: the one-rank partial is the whole attention."""
+    rng = np.random.default_rng(11 + heads + q_len)
+    lengths = tuple(int(x) for x in rng.integers(q_len, 41, size=160))
+    if kind == "mla":
+        wl = di.Workload("short_mla", "mla", 160, heads, 1, 576, 512, 64, 1, 1, 41, lengths)
+    else:
+        wl = di.Workload("short_gqa", "gqa", 160, heads, 4, 128, 128, 16, 1, 1, 43, lengths)
+    B = wl.batch
+    if q_len == 1:
+        o, lse, _ = run_rank(wl, 0)
+        o, lse = o.view(B, 1, heads, wl.v_dim), lse.view(B, 1, heads)
+    else:
+        o, lse = run_rank_mtp(wl, 0, q_len)
+    on, ln = o.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        if q_len == 1:
+            o_ref, l_ref = oracle.full_attention(wl, b)
+            o_ref, l_ref = o_ref[None], l_ref[None]
+        else:
+            o_ref, l_ref = oracle.mtp_full_attention(wl, b, q_len)
+        check_close(on[b], ln[b], o_ref, l_ref, "short %s H%d q%d b=%d" % (kind, heads, q_len, b), tol_o=1e-3)
 
 
 @pytest.mark.parametrize("kind", ["mla", "gqa"])
