@@ -468,8 +468,7 @@ __global__ __launch_bounds__(128 * NH, 1) void mla_partial_kernel(PartialParams 
 //    block x k-step parity), runs the online softmax and leaves P^T (bf16, laid out
 //    as the MFMA B operand), the rescale factor of each head and, at the end of a
 //    piece, 1/l in LDS; it stores the piece's LSE itself.  In a tile where its head
-//    block needs them it also leaves the low parts of P (fp8-coded), and says so in
-//    the sign of the block's rescale factors.
+//    block needs them it also leaves the low parts of P (fp8-coded) and a flag.
 //  * P.V waves 4..11: wave v owns output dims 64 v .. 64 v + 63 of all 64 heads
 //    (16 O^T accumulators of 16 dims x 16 heads).  During tile j's interval it
 //    rescales, accumulates O^T += V^T P^T for tile j (a second pass adds the low
@@ -515,6 +514,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
   __shared__ __attribute__((aligned(16))) u32x2 s_pl[2][kHeadBlocks][64];   // the low parts, fp8-coded
   __shared__ __attribute__((aligned(16))) float s_alpha[2][16][kHeadBlocks];  // [parity][head in block][block]
   __shared__ __attribute__((aligned(16))) float s_inv[2][16][kHeadBlocks];
+  __shared__ __attribute__((aligned(16))) int s_lo[2][kHeadBlocks];  // head block's tile took the low parts
   __shared__ int64_t s_loc[4];
 
   const int tid = threadIdx.x;
@@ -628,6 +628,13 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
       const Cursor cur = sc;
       const int par = j & 1;
       const DCP_LDS uint8_t* tb = lds + (j % kStages) * kTileBytes;
+      // The head block's tile takes the low parts of its weights (see kLowShare) if one
+      // of them is above kLowShare of the row sum after the tile.  That sum is at least
+      // the sum before the tile (rescaled) plus the weight itself, so a weight P of it
+      // qualifies if P (1 - kLowShare) > kLowShare l_prev alpha, which flags every tile
+      // that needs it: in log2 units against the running maximum, log2 P > lo_thr.  The
+      // threshold's cross-lane adds and logarithm overlap the score MFMAs.
+      float lo_thr = fast_log2(kLowShare / (1.f - kLowShare) * sum_over_groups(l_run));
       f32x4 s0, s1;
       qk(tb, s0, s1);
       if (j + 1 < total) {
@@ -665,6 +672,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
         const float m_new = mh > m_run + kRescaleSlack ? mh : m_run;
         // no visible token yet (a causally masked row): nothing to weigh or rescale
         alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+        lo_thr += m_new == -INFINITY ? 0.f : m_run - m_new;  // log2(alpha)
         l_run *= alpha;
         m_run = m_new;
       }
@@ -677,21 +685,22 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
         pb[e] = (__bf16)pr;
       }
       s_p[par][sb][lane] = pb;
-      // the head block's tile takes the low parts of its weights (see kLowShare); the
-      // P.V waves read that from the sign of the block's rescale factors
-      const float l_tot = sum_over_groups(l_run);
-      const float pmax = none ? 0.f : fast_exp2(mloc - m_run);
-      const bool need_lo = cur.Lr <= kLowAllTokens || __any(pmax > kLowShare * l_tot);
+      // (a row with no visible token has mloc - m_run = NaN: never flagged)
+      const bool need_lo = cur.Lr <= kLowAllTokens || __any(mloc - m_run > lo_thr);
+      if (q4 == 0) {
+        s_alpha[par][l16][sb] = alpha;
+        s_lo[par][sb] = need_lo;  // the same value from the 16 lanes
+      }
       if (need_lo) {
         float lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) lo[e] = (none ? 0.f : fast_exp2(x[e] - m_run)) - (float)pb[e];
         s_pl[par][sb][lane] = code_low_parts(lo);
       }
-      if (q4 == 0) s_alpha[par][l16][sb] = need_lo ? -alpha : alpha;
       if (cur.t == cur.ntile - 1 || j == total - 1) {
         bool whole;
         const int64_t row = piece_row(pc, cur, head_ok ? head : 0, whole);
+        const float l_tot = sum_over_groups(l_run);
         if (q4 == 0) {
           // a row that saw no token of the piece: O = 0, LSE = -inf
           s_inv[par][l16][sb] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
@@ -823,12 +832,10 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
           for (int e = lane; e < n; e += 64)
             zero_lds16(lds_addr(tb + (nvalid + e / kC) * kRowBytes + (kC * v + e % kC) * 16));
         }
-        // rescale factors of the four head blocks; a set sign bit asks for the low parts
-        const f32x4 araw = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
-        const u32x4 abits = __builtin_bit_cast(u32x4, araw);
-        const int lo_blocks = uniform((int)((abits[0] >> 31) | (abits[1] >> 31) << 1 | (abits[2] >> 31) << 2 |
-                                            (abits[3] >> 31) << 3));
-        const f32x4 alpha = __builtin_bit_cast(f32x4, abits & 0x7FFFFFFFu);
+        const f32x4 alpha = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
+        // the head blocks whose tile takes the low parts of its weights
+        const i32x4 lo_flags = *(const DCP_LDS i32x4*)&s_lo[par][0];
+        const int lo_blocks = uniform(lo_flags[0] | lo_flags[1] << 1 | lo_flags[2] << 2 | lo_flags[3] << 3);
         bf16x8 pP[kHeadBlocks];
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocks; ++hb) pP[hb] = s_p[par][hb][lane];
