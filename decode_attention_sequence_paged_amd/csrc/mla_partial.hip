@@ -514,7 +514,7 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
   __shared__ __attribute__((aligned(16))) u32x2 s_pl[2][kHeadBlocks][64];   // the low parts, fp8-coded
   __shared__ __attribute__((aligned(16))) float s_alpha[2][16][kHeadBlocks];  // [parity][head in block][block]
   __shared__ __attribute__((aligned(16))) float s_inv[2][16][kHeadBlocks];
-  __shared__ __attribute__((aligned(16))) int s_lo[2][kHeadBlocks];  // head block's tile took the low parts
+  __shared__ __attribute__((aligned(16))) int s_lo[2][16][kHeadBlocks];  // the head block's tile took the low parts
   __shared__ int64_t s_loc[4];
 
   const int tid = threadIdx.x;
@@ -677,6 +677,12 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
         m_run = m_new;
       }
       const bool none = m_run == -INFINITY;
+      // (a row with no visible token has mloc - m_run = NaN: never flagged)
+      const bool need_lo = cur.Lr <= kLowAllTokens || __any(mloc - m_run > lo_thr);
+      if (q4 == 0) {
+        s_alpha[par][l16][sb] = alpha;
+        s_lo[par][l16][sb] = need_lo;
+      }
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -685,12 +691,6 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
         pb[e] = (__bf16)pr;
       }
       s_p[par][sb][lane] = pb;
-      // (a row with no visible token has mloc - m_run = NaN: never flagged)
-      const bool need_lo = cur.Lr <= kLowAllTokens || __any(mloc - m_run > lo_thr);
-      if (q4 == 0) {
-        s_alpha[par][l16][sb] = alpha;
-        s_lo[par][sb] = need_lo;  // the same value from the 16 lanes
-      }
       if (need_lo) {
         float lo[8];
 #pragma unroll
@@ -833,9 +833,10 @@ __global__ __launch_bounds__(wide::PV<kPV>::kThreads, 1) void mla_partial_wide_k
             zero_lds16(lds_addr(tb + (nvalid + e / kC) * kRowBytes + (kC * v + e % kC) * 16));
         }
         const f32x4 alpha = *(const DCP_LDS f32x4*)&s_alpha[par][l16][0];
-        // the head blocks whose tile takes the low parts of its weights
-        const i32x4 lo_flags = *(const DCP_LDS i32x4*)&s_lo[par][0];
-        const int lo_blocks = uniform(lo_flags[0] | lo_flags[1] << 1 | lo_flags[2] << 2 | lo_flags[3] << 3);
+        // the head blocks whose tile takes the low parts of its weights (the same in every lane)
+        const i32x4 lo_flags = *(const DCP_LDS i32x4*)&s_lo[par][l16][0];
+        // (kept a vector value: a scalar copy would wait for this read before the pass below)
+        const int lo_blocks = lo_flags[0] | lo_flags[1] << 1 | lo_flags[2] << 2 | lo_flags[3] << 3;
         bf16x8 pP[kHeadBlocks];
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocks; ++hb) pP[hb] = s_p[par][hb][lane];
