@@ -194,6 +194,11 @@ size_t dcp_decode_workspace_size(const dcp_attn_desc_t* desc, int32_t batch,
  *   out_lse      device fp32 [batch, H], written: LSE_r = ln sum_t exp(s_t),
  *                s_t = softmax_scale * (q . k_t).
  *   A request with no local tokens gets O_r = 0 and LSE_r = -inf.
+ * Arithmetic: scores, softmax statistics and accumulation in fp32; the softmax
+ * weights enter the P.V product as bf16, plus their bf16 low part in the tiles
+ * where a weight is a sizeable share of its row (requests of up to 256 local
+ * tokens, dominant tokens), which keeps |dO| against exact attention near 1e-3
+ * or below on bf16 inputs of unit scale.
  * Supported: MLA with qk_dim 576, v_dim 512, 1 <= H <= 512, block_size a
  * multiple of 32; GQA with qk_dim = v_dim = 128, H / num_kv_heads <= 16,
  * block_size a multiple of 16.
