@@ -676,6 +676,11 @@ MTP_CASES = [
                         lengths=(300, 5, 6, 7, 129))),
     ("gqa_b32", 7, dict(num_q_heads=64, num_kv_heads=8, dcp_size=3, interleave=2, block_size=64,
                         lengths=(1500, 6, 7, 8, 9, 65))),
+    # the largest shapes: 512 MLA score rows (eight 64-row groups) and 64 GQA query tokens
+    # (sixteen passes of four)
+    ("mla_long_b128", 8, dict(batch=2, lengths=(3000, 1025))),
+    ("gqa_b32", 64, dict(num_q_heads=8, num_kv_heads=2, dcp_size=2, interleave=4, block_size=16,
+                         lengths=(300, 64, 70))),
 ]
 
 
