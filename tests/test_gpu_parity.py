@@ -444,11 +444,12 @@ def test_full_size_1m_every_rank_and_merge():
     check_close(om[0], lm[0], Of, Lf, "1m merged")
 
 
-@pytest.mark.parametrize("name", ["mla_1m", "mla_long_b128"])
+@pytest.mark.parametrize("name", ["mla_1m", "mla_long_b128", "mla_c512"])
 def test_full_size_census_rank0(name):
     """Census at the full shape in the benchmark's launch configuration: rank 0 of the
     1M-token request (131,072 local tokens cut over every work partition and merged by the
-    split-K path) and of the 128-request batch; the exact token set of every request."""
+    split-K path) and of the 128- and 512-request batches; the exact token set of every
+    request."""
     _census_check(di.WORKLOADS[name], ranks=[0])
 
 
