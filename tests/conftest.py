@@ -12,6 +12,19 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+@pytest.fixture(scope="session", autouse=True)
+def _built_libraries():
+    """Build the in-tree libraries once if they are missing (a fresh checkout keeps no built
+    files); a tree that has them is used as it is."""
+    from decode_attention_sequence_paged_amd import build as pkg_build
+    from dcp_inputs import HOST_LIB_PATH, SYNTH_LIB_PATH
+    from dcp_inputs import build as inputs_build
+    if not os.path.exists(pkg_build.LIB_PATH):
+        pkg_build.build_lib()
+    if not (os.path.exists(HOST_LIB_PATH) and os.path.exists(SYNTH_LIB_PATH)):
+        inputs_build.build_all()
+
+
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped, not failed, where no GPU is visible (e.g. CPU-only runs).
     try:
