@@ -67,6 +67,36 @@ int main(void) {
         "workspace_errors: short workspace rejected");
   check(dcp_workspace_errors(f, 4096, NULL, 0, NULL) == DCP_ERROR_INVALID_VALUE,
         "workspace_errors: NULL output rejected");
+  /* Multi-token sizing and checks. */
+  const size_t ws1 = dcp_decode_workspace_size(&mla, 128, 256);
+  check(dcp_decode_workspace_size_mtp(&mla, 1, 128, 256) == ws1, "mtp: q_len 1 sizes like the decode call");
+  check(dcp_decode_workspace_size_mtp(&mla, 2, 128, 256) > ws1, "mtp: two query tokens need more workspace");
+  check(dcp_decode_workspace_size_mtp(&mla, 0, 128, 256) == 0, "mtp: q_len 0 gives no workspace");
+  check(dcp_decode_workspace_size_mtp(&mla, 9, 128, 256) == 0, "mtp: more than 512 MLA score rows unsupported");
+  check(dcp_decode_partial_mtp(&mla, 0, f, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 0, 2, 1, 0,
+                               f, 1 << 30, (float*)f, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
+        "mtp: q_len 0 rejected before launch");
+  /* The allocation-free call checks its arguments before touching its scratch. */
+  check(dcp_decode_partial_noalloc(&mla, f, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 2, 2, 1,
+                                   0, (float*)f, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
+        "noalloc: rank >= N rejected before launch");
+  /* KV append, local block table and the per-rank merge steps: argument checks. */
+  check(dcp_append_kv(&mla, f, NULL, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 0, 0, 1, NULL) ==
+            DCP_ERROR_INVALID_VALUE,
+        "append: N = 0 rejected");
+  check(dcp_append_kv(&mla, f, f, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 0, 2, 1, NULL) ==
+            DCP_ERROR_INVALID_VALUE,
+        "append: an MLA V pointer rejected");
+  check(dcp_local_block_table((const int32_t*)f, 2, 8, 2, 100, 64, 0, (int32_t*)f, 4, NULL) ==
+            DCP_ERROR_NOT_SUPPORTED,
+        "local block table: interleave not a multiple of the page size unsupported");
+  check(dcp_merge_lse((const float*)f, 0, 2, 4, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
+        "merge_lse: zero parts rejected");
+  check(dcp_rescale_partial((const float*)f, (const float*)f, (const float*)f, 2, 4, 512, 7, f, NULL) ==
+            DCP_ERROR_INVALID_VALUE,
+        "rescale: unknown transport dtype rejected");
+  check(dcp_sum_head_slice(f, DCP_DTYPE_F32, 3, 2, 4, 512, 0, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
+        "sum_head_slice: heads not divisible by the ranks rejected");
   printf("%d failures\n", failures);
   return failures != 0;
 }
