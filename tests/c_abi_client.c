@@ -76,10 +76,12 @@ int main(void) {
   check(dcp_decode_partial_mtp(&mla, 0, f, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 0, 2, 1, 0,
                                f, 1 << 30, (float*)f, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
         "mtp: q_len 0 rejected before launch");
+#ifndef DCP_CLIENT_HOST_ONLY
   /* The allocation-free call checks its arguments before touching its scratch. */
   check(dcp_decode_partial_noalloc(&mla, f, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 2, 2, 1,
                                    0, (float*)f, (float*)f, NULL) == DCP_ERROR_INVALID_VALUE,
         "noalloc: rank >= N rejected before launch");
+#endif
   /* KV append, local block table and the per-rank merge steps: argument checks. */
   check(dcp_append_kv(&mla, f, NULL, f, NULL, 10, (const int32_t*)f, 4, (const int32_t*)f, 2, 0, 0, 1, NULL) ==
             DCP_ERROR_INVALID_VALUE,
